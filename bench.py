@@ -1,0 +1,244 @@
+"""Benchmark of the MoE dispatch/combine hot path on one MI355X.
+
+One step = one pass of the whole path over one layer's batch:
+  moe_route_build (multihot map, counts, padded offsets, rows of slots; the
+  eager readback included) + moe_dispatch + moe_combine + moe_combine_bwd
+  (cached dispatch of grad_out plus the routing-weight gradients).
+
+Protocol (after the benchmark section of "Add the deepep expert-parallel
+implementation": distinct layers back to back, median of windows):
+  * `--sets` (default 4) independent layer buffer sets, each with its own
+    routing, rotated step by step so a step's inputs were last touched several
+    hundred MB of traffic earlier (MI355X's 256 MB Infinity Cache);
+  * combine reads a separate expert-output buffer (a stand-in for the grouped
+    GEMM output), which also serves as the expert output of the backward;
+  * W warm-up steps, then K timed steps between two device synchronizations;
+    each kernel is also bracketed by HIP events on the launch stream.
+
+Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
+the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
+(event-timed) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs/layer and achieved HBM GB/s (% peak), 4096 & 16384 tok"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def byte_model(wl, tpe_total_valid, R, n_active, idx_bytes, with_probs):
+    """Algorithmic bytes per launch (each input read once, each output written once)."""
+    T, H, k, E = wl.T, wl.H, wl.k, wl.E
+    EL = wl.num_local
+    row = 2 * H
+    route = (T * k * idx_bytes + T * E            # ids in, multihot map out
+             + (T * k * 4 + T * E * 4 if with_probs else 0)  # weights in, probs out
+             + T * k * 4                           # row_of_slot out
+             + (2 * EL + 1) * 4 + 16)              # counts, offsets, status
+    dispatch = (n_active * row + T * k * 4 * 2     # active token rows, weights, row_of_slot
+                + R * row + R * 12)                # rows out + row_w/row_token/row_expert
+    combine = tpe_total_valid * row + T * k * 4 + T * row
+    bwd = (n_active * row + tpe_total_valid * row  # grad_out rows in, expert rows in
+           + T * k * 4 + R * row + T * k * 4)      # row_of_slot, grad rows out, dw out
+    return {"route": route, "dispatch": dispatch, "combine": combine, "combine_bwd": bwd}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b")
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall budget of the oracle CPU-baseline leg (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only (no inter-GPU exchange is built); "
+              f"--gpus {args.gpus} is not supported, run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from combine_topk_idx_multihot_amd import binding as B
+    from combine_topk_idx_multihot_amd import inputs
+
+    wl = inputs.WORKLOADS[args.workload]
+    seed0 = args.seed if args.seed is not None else 1000 + list(inputs.WORKLOADS).index(wl.name) + 1
+    dev = torch.device("cuda:0")
+    B.moe_device_check(0)
+    stream = torch.cuda.current_stream()
+    EL = wl.num_local
+    mode = B.MOE_SYNC_FREE if wl.sync_free else B.MOE_EAGER
+    d = B.make_desc(wl.T, wl.k, wl.E, wl.lb, EL, wl.P, mode, False, wl.cap if wl.sync_free else 0)
+    Rmax = B.moe_capacity_min(d) if not wl.sync_free else wl.cap
+    H = wl.H
+
+    # ---- buffer sets -------------------------------------------------------
+    sets = []
+    gen = torch.Generator(device=dev)
+    for s in range(args.sets):
+        idx, w = inputs.make_routing(wl, seed0 + 7919 * s)
+        gen.manual_seed(seed0 * 31 + s)
+        st = {
+            "idx_np": idx, "w_np": w,
+            "idx": torch.from_numpy(idx).to(dev), "w": torch.from_numpy(w).to(dev),
+            "x": torch.randn((wl.T, H), generator=gen, device=dev).to(torch.bfloat16),
+            "g": torch.randn((wl.T, H), generator=gen, device=dev).to(torch.bfloat16),
+            "Y": torch.randn((Rmax, H), generator=gen, device=dev).to(torch.bfloat16),
+            "rows": torch.empty((Rmax, H), dtype=torch.bfloat16, device=dev),
+            "grad_rows": torch.empty((Rmax, H), dtype=torch.bfloat16, device=dev),
+            "row_w": torch.empty(Rmax, dtype=torch.float32, device=dev),
+            "row_token": torch.empty(Rmax, dtype=torch.int32, device=dev),
+            "row_expert": torch.empty(Rmax, dtype=torch.int32, device=dev),
+            "out": torch.empty((wl.T, H), dtype=torch.bfloat16, device=dev),
+            "dw": torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev),
+            "probs": torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev),
+            "h": B.alloc_handle(d, dev),
+            "ws": B.workspace_for(d, dev),
+        }
+        sets.append(st)
+    torch.cuda.synchronize()
+
+    names = ("route", "dispatch", "combine", "combine_bwd")
+
+    def step(st, events=None):
+        ev = events
+        if ev is not None:
+            ev[0].record(stream)
+        B.moe_route_build(d, st["idx"], st["h"], st["ws"], st["w"], st["probs"], stream=stream)
+        R = wl.cap if wl.sync_free else st["h"].total
+        if ev is not None:
+            ev[1].record(stream)
+        B.moe_dispatch(d, st["h"], st["x"], H, R, st["rows"], st["w"], st["row_w"],
+                       st["row_token"], st["row_expert"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["Y"], st["dw"],
+                          stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+        return R
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # per-set routing facts for the byte model (from the warmed handles)
+    facts = []
+    for st in sets:
+        step(st)
+        torch.cuda.synchronize()
+        hs = st["h"].status.cpu().numpy()
+        idx = st["idx_np"]
+        local = (idx >= wl.lb) & (idx < wl.lb + EL)
+        n_active = int(local.any(axis=1).sum())
+        R = wl.cap if wl.sync_free else int(hs[0])
+        facts.append(byte_model(wl, int(hs[2]), R, n_active, 4, True) | {"R": R})
+
+    # timed region
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_kernel_ms = {n: [] for n in names}
+    bytes_sum = {n: 0 for n in names}
+    for i in range(args.steps):
+        f = facts[i % len(sets)]
+        for j, n in enumerate(names):
+            per_kernel_ms[n].append(evs[i][j].elapsed_time(evs[i][j + 1]))
+            bytes_sum[n] += f[n]
+    kern = {}
+    for n in names:
+        avg_ms = float(np.mean(per_kernel_ms[n]))
+        avg_bytes = bytes_sum[n] / args.steps
+        kern[n] = {"avg_us": round(avg_ms * 1e3, 2), "median_us": round(float(np.median(per_kernel_ms[n])) * 1e3, 2),
+                   "alg_bytes": int(avg_bytes), "GBps": round(avg_bytes / (avg_ms * 1e-3) / 1e9, 1)}
+    step_bytes = sum(bytes_sum.values()) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda n: kern[n]["avg_us"])
+    dev_us = sum(kern[n]["avg_us"] for n in names)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": H, "E": wl.E, "k": wl.k,
+                   "local_experts": EL, "pad_multiple": wl.P,
+                   "mode": "sync_free" if wl.sync_free else "eager",
+                   "rows": int(np.mean([f["R"] for f in facts])), "buffer_sets": args.sets},
+        "us_per_layer": {"forward_device": round(kern["route"]["avg_us"] + kern["dispatch"]["avg_us"] + kern["combine"]["avg_us"], 2),
+                         "backward_device": kern["combine_bwd"]["avg_us"],
+                         "step_wall": round(ms_per_step * 1e3, 2), "step_device": round(dev_us, 2)},
+        "kernels": kern,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": kern[dominant]["GBps"],
+                     "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kern[dominant]["GBps"] / PEAK_GBS, 4), "traffic": None},
+    }
+
+    # ---- CPU baseline: the oracle on the host, bounded sample ---------------
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, sets[0], args.cpu_seconds, torch)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, st, budget_s, torch):
+    import oracle
+
+    idx, w = st["idx_np"], st["w_np"]
+    u16 = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    x, g = u16(st["x"]), u16(st["g"])
+    EL = wl.num_local
+    C = wl.cap if wl.sync_free else 0
+    Y = u16(st["Y"])
+    reps, t_used, bytes_done = 0, 0.0, 0
+    while t_used < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        r = oracle.route(idx, wl.E, wl.lb, EL, wl.P, sync_free=wl.sync_free, C=C, w=w, x=x,
+                         want_probs=True)
+        oracle.combine(idx, r.row_of_slot, Y[:r.R], wl.E, wl.lb, EL)
+        oracle.combine_bwd(idx, r.row_of_slot, r.row_token, g, wl.E, wl.lb, EL, F=Y[:r.R], R=r.R)
+        t_used += time.perf_counter() - t0
+        local = (idx >= wl.lb) & (idx < wl.lb + EL)
+        bm = byte_model(wl, int(r.tpe.sum()), r.R, int(local.any(axis=1).sum()), 4, True)
+        bytes_done += sum(bm.values())
+        reps += 1
+    return {"value": round(bytes_done / t_used / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "ms_per_step": round(t_used * 1e3 / reps, 1),
+            "sample": f"{reps} full step(s) of the {wl.name} layer (route+dispatch+combine+"
+                      f"combine_bwd with dw), single-threaded C oracle, {t_used:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

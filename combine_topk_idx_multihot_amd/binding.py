@@ -1,0 +1,311 @@
+"""Thin Python binding of libmoe_mi355x (C ABI in include/moe_mi355x.h).
+
+Argument marshalling only: torch supplies device memory and streams, every step
+of the path runs in the library's HIP kernels.  The ``moe_*`` functions mirror
+the C entry points one for one; before passing a pointer they check that each
+tensor lives on the GPU, is contiguous, has the expected dtype and is large
+enough for what the call will write (the C ABI takes plain pointers and cannot).
+The convenience functions at the bottom (``alloc_handle``, ``route``,
+``dispatch``, ``combine``, ``combine_bwd``) only add output allocation.
+
+The library is loaded on first use; if it has not been built this raises
+(there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_HIDDEN, MOE_ERR_CAPACITY = 0, 1, 2, 3
+MOE_ERR_WORKSPACE, MOE_ERR_INDEX, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
+MOE_EAGER, MOE_SYNC_FREE = 0, 1
+MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
+
+# Every symbol include/moe_mi355x.h declares.
+EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build", "moe_dispatch",
+           "moe_combine", "moe_combine_bwd", "moe_last_error", "moe_device_check")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[moe status {code}] {msg}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("k", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("local_begin", ctypes.c_int32), ("num_local", ctypes.c_int32),
+                ("pad_multiple", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("idx_is_i64", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("capacity", ctypes.c_int64)]
+
+
+class _Handle(ctypes.Structure):
+    _fields_ = [("routing_map", ctypes.c_void_p), ("tokens_per_expert", ctypes.c_void_p),
+                ("padded_offsets", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p),
+                ("status", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe_mi355x.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m combine_topk_idx_multihot_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        pd, ph = ctypes.POINTER(Desc), ctypes.POINTER(_Handle)
+        L.moe_capacity_min.argtypes = [pd]
+        L.moe_capacity_min.restype = i64
+        L.moe_route_workspace_size.argtypes = [pd]
+        L.moe_route_workspace_size.restype = ctypes.c_size_t
+        L.moe_route_build.argtypes = [pd, vp, vp, vp, ph, vp, ctypes.c_size_t, vp, vp]
+        L.moe_route_build.restype = ctypes.c_int
+        L.moe_dispatch.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp]
+        L.moe_dispatch.restype = ctypes.c_int
+        L.moe_combine.argtypes = [pd, ph, vp, i32, i64, vp, i32, vp]
+        L.moe_combine.restype = ctypes.c_int
+        L.moe_combine_bwd.argtypes = [pd, ph, vp, vp, i32, i64, vp, vp, vp]
+        L.moe_combine_bwd.restype = ctypes.c_int
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_device_check.argtypes = [ctypes.c_int]
+        L.moe_device_check.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        raise MoeError(rc, last_error())
+    return rc
+
+
+def make_desc(T: int, k: int, E: int, local_begin: int = 0, num_local: int | None = None,
+              pad_multiple: int = 1, mode: int = MOE_EAGER, idx_is_i64: bool = False,
+              capacity: int = 0) -> Desc:
+    return Desc(T=T, k=k, E=E, local_begin=local_begin,
+                num_local=E if num_local is None else num_local, pad_multiple=pad_multiple,
+                mode=mode, idx_is_i64=int(bool(idx_is_i64)), reserved=0, capacity=capacity)
+
+
+# ---------------------------------------------------------------------------
+# tensor checks (the C ABI cannot see buffer sizes)
+# ---------------------------------------------------------------------------
+
+def _dev(t: torch.Tensor | None, name: str, dtype, numel: int, optional: bool = False):
+    if t is None:
+        if optional:
+            return None
+        raise MoeError(MOE_ERR_ARG, f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeError(MOE_ERR_ARG, f"{name} must be a GPU tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise MoeError(MOE_ERR_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise MoeError(MOE_ERR_ARG, f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise MoeError(MOE_ERR_ARG, f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+@dataclass
+class Handle:
+    """Dispatch handle: plain device tensors plus a pinned host status."""
+    desc: Desc
+    routing_map: torch.Tensor | None   # [T,E] uint8
+    tokens_per_expert: torch.Tensor    # [EL] int32
+    padded_offsets: torch.Tensor       # [EL+1] int32
+    row_of_slot: torch.Tensor          # [T,k] int32
+    status: torch.Tensor               # [4] int32 (device)
+    host_status: torch.Tensor          # [4] int32 (pinned host)
+
+    def c(self) -> _Handle:
+        d = self.desc
+        return _Handle(
+            routing_map=_dev(self.routing_map, "routing_map", torch.uint8, d.T * d.E, True),
+            tokens_per_expert=_dev(self.tokens_per_expert, "tokens_per_expert", torch.int32,
+                                   d.num_local),
+            padded_offsets=_dev(self.padded_offsets, "padded_offsets", torch.int32,
+                                d.num_local + 1),
+            row_of_slot=_dev(self.row_of_slot, "row_of_slot", torch.int32, d.T * d.k),
+            status=_dev(self.status, "status", torch.int32, 4))
+
+    @property
+    def total(self) -> int:
+        """Padded row total from the last eager moe_route_build."""
+        return int(self.host_status[0])
+
+    @property
+    def flags(self) -> int:
+        return int(self.host_status[1])
+
+
+def alloc_handle(desc: Desc, device="cuda", with_map: bool = True) -> Handle:
+    T, E, EL, k = desc.T, desc.E, desc.num_local, desc.k
+    return Handle(
+        desc=desc,
+        routing_map=torch.empty((T, E), dtype=torch.uint8, device=device) if with_map else None,
+        tokens_per_expert=torch.empty(EL, dtype=torch.int32, device=device),
+        padded_offsets=torch.empty(EL + 1, dtype=torch.int32, device=device),
+        row_of_slot=torch.empty((T, k), dtype=torch.int32, device=device),
+        status=torch.empty(4, dtype=torch.int32, device=device),
+        host_status=torch.zeros(4, dtype=torch.int32, pin_memory=True))
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one for one
+# ---------------------------------------------------------------------------
+
+def moe_capacity_min(desc: Desc) -> int:
+    return int(lib().moe_capacity_min(ctypes.byref(desc)))
+
+
+def moe_route_workspace_size(desc: Desc) -> int:
+    n = int(lib().moe_route_workspace_size(ctypes.byref(desc)))
+    if n == 0:
+        raise MoeError(MOE_ERR_ARG, last_error())
+    return n
+
+
+def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle, workspace: torch.Tensor,
+                    topk_w: torch.Tensor | None = None, multihot_probs: torch.Tensor | None = None,
+                    stream=None) -> int:
+    """Returns MOE_OK; eager mode fills handle.host_status (total, flags, data rows)."""
+    n = desc.T * desc.k
+    idx_dtype = torch.int64 if desc.idx_is_i64 else torch.int32
+    p_idx = _dev(topk_idx, "topk_idx", idx_dtype, n) if n else None
+    p_w = _dev(topk_w, "topk_w", torch.float32, n, optional=True)
+    p_probs = _dev(multihot_probs, "multihot_probs", torch.float32, desc.T * desc.E, optional=True)
+    p_ws = _dev(workspace, "workspace", torch.uint8, 0)
+    ws_bytes = workspace.numel()
+    hs = handle.host_status
+    if hs.is_cuda or hs.dtype != torch.int32 or hs.numel() < 4:
+        raise MoeError(MOE_ERR_ARG, "host_status must be a host int32 tensor of 4 elements")
+    h = handle.c()
+    return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, ctypes.byref(h),
+                                        p_ws, ws_bytes, hs.data_ptr(), _stream(stream)))
+
+
+def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, rows: torch.Tensor,
+                 topk_w: torch.Tensor | None = None, row_w: torch.Tensor | None = None,
+                 row_token: torch.Tensor | None = None, row_expert: torch.Tensor | None = None,
+                 stream=None) -> int:
+    p_x = _dev(x, "x", torch.bfloat16, desc.T * H) if desc.T else None
+    p_rows = _dev(rows, "rows", torch.bfloat16, R * H) if R else None
+    p_w = _dev(topk_w, "topk_w", torch.float32, desc.T * desc.k, optional=True)
+    p_rw = _dev(row_w, "row_w", torch.float32, R, optional=True)
+    if desc.T == 0:
+        p_w = None
+    if R == 0:
+        p_rw = None
+        if p_w is not None:  # no row to weight; the C ABI pairs the two pointers
+            p_w = None
+    p_rt = _dev(row_token, "row_token", torch.int32, R, optional=True)
+    p_re = _dev(row_expert, "row_expert", torch.int32, R, optional=True)
+    h = handle.c()
+    return _check(lib().moe_dispatch(ctypes.byref(desc), ctypes.byref(h), p_x, H, p_w, R, p_rows,
+                                     p_rw, p_rt, p_re, _stream(stream)))
+
+
+def moe_combine(desc: Desc, handle: Handle, Y: torch.Tensor, H: int, R: int, out: torch.Tensor,
+                stream=None) -> int:
+    out_f32 = out.dtype == torch.float32
+    p_y = _dev(Y, "Y", torch.bfloat16, R * H) if R else None
+    p_o = _dev(out, "out", (torch.bfloat16, torch.float32), desc.T * H) if desc.T else None
+    h = handle.c()
+    return _check(lib().moe_combine(ctypes.byref(desc), ctypes.byref(h), p_y, H, R, p_o,
+                                    int(out_f32), _stream(stream)))
+
+
+def moe_combine_bwd(desc: Desc, handle: Handle, grad_out: torch.Tensor, H: int, R: int,
+                    grad_rows: torch.Tensor, expert_out: torch.Tensor | None = None,
+                    dw: torch.Tensor | None = None, stream=None) -> int:
+    p_g = _dev(grad_out, "grad_out", torch.bfloat16, desc.T * H) if desc.T else None
+    p_gr = _dev(grad_rows, "grad_rows", torch.bfloat16, R * H) if R else None
+    p_f = _dev(expert_out, "expert_out", torch.bfloat16, R * H, optional=True) if R else None
+    p_dw = _dev(dw, "dw", torch.float32, desc.T * desc.k, optional=True)
+    if desc.T == 0:  # no slot: nothing for dw to hold, expert_out is not read
+        p_f = p_dw = None
+    h = handle.c()
+    return _check(lib().moe_combine_bwd(ctypes.byref(desc), ctypes.byref(h), p_g, p_f, H, R, p_gr,
+                                        p_dw, _stream(stream)))
+
+
+def moe_device_check(device: int = 0) -> int:
+    return _check(lib().moe_device_check(device))
+
+
+# ---------------------------------------------------------------------------
+# convenience wrappers that allocate outputs
+# ---------------------------------------------------------------------------
+
+def workspace_for(desc: Desc, device="cuda") -> torch.Tensor:
+    return torch.empty(moe_route_workspace_size(desc), dtype=torch.uint8, device=device)
+
+
+def route(desc: Desc, topk_idx: torch.Tensor, topk_w: torch.Tensor | None = None,
+          want_probs: bool = False, with_map: bool = True, handle: Handle | None = None,
+          workspace: torch.Tensor | None = None, stream=None):
+    """moe_route_build with fresh outputs.  Returns (handle, multihot_probs or None)."""
+    dev = topk_idx.device
+    handle = handle or alloc_handle(desc, dev, with_map=with_map)
+    workspace = workspace if workspace is not None else workspace_for(desc, dev)
+    probs = torch.empty((desc.T, desc.E), dtype=torch.float32, device=dev) if want_probs else None
+    moe_route_build(desc, topk_idx, handle, workspace, topk_w if want_probs else None, probs,
+                    stream=stream)
+    return handle, probs
+
+
+def rows_for(desc: Desc, handle: Handle) -> int:
+    return desc.capacity if desc.mode == MOE_SYNC_FREE else handle.total
+
+
+def dispatch(desc: Desc, handle: Handle, x: torch.Tensor, topk_w: torch.Tensor | None = None,
+             meta: bool = True, stream=None):
+    """moe_dispatch with fresh outputs: (rows, row_w, row_token, row_expert)."""
+    R, H, dev = rows_for(desc, handle), x.shape[1], x.device
+    rows = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    row_w = torch.empty(R, dtype=torch.float32, device=dev) if topk_w is not None else None
+    rt = torch.empty(R, dtype=torch.int32, device=dev) if meta else None
+    re = torch.empty(R, dtype=torch.int32, device=dev) if meta else None
+    moe_dispatch(desc, handle, x, H, R, rows, topk_w, row_w, rt, re, stream=stream)
+    return rows, row_w, rt, re
+
+
+def combine(desc: Desc, handle: Handle, Y: torch.Tensor, out_dtype=torch.bfloat16, stream=None):
+    R, H = Y.shape
+    out = torch.empty((desc.T, H), dtype=out_dtype, device=Y.device)
+    moe_combine(desc, handle, Y, H, R, out, stream=stream)
+    return out
+
+
+def combine_bwd(desc: Desc, handle: Handle, grad_out: torch.Tensor, R: int,
+                expert_out: torch.Tensor | None = None, stream=None):
+    H, dev = grad_out.shape[1], grad_out.device
+    grad_rows = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((desc.T, desc.k), dtype=torch.float32, device=dev) if expert_out is not None else None
+    moe_combine_bwd(desc, handle, grad_out, H, R, grad_rows, expert_out, dw, stream=stream)
+    return grad_rows, dw

@@ -1,0 +1,391 @@
+// api.hip -- the C ABI of libmoe_mi355x (declared in include/moe_mi355x.h).
+//
+// Host side only: argument checks (all before any launch), launch geometry,
+// and the one host readback of eager routing.  Requirements it enforces come
+// from "Add the deepep expert-parallel implementation": hidden size a
+// multiple of 256 (requirements paragraph), worst-case sync-free capacity
+// ("Eager vs captured"), nothing allocated and no sync on the sync-free path
+// ("Buffers", "Custom ops"); and from the review on "feat: add hybridep" that
+// accepted flags must not be silently ignored (every optional argument either
+// takes effect or is rejected).
+#include "moe_mi355x.h"
+#include "moe_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return MOE_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cap_min(const moe_desc *d)
+{
+    const int64_t kk = d->k < d->num_local ? d->k : d->num_local;
+    return d->T * kk + static_cast<int64_t>(d->num_local) * (d->pad_multiple - 1);
+}
+
+constexpr int64_t kI32Max = 2147483647;
+
+int check_desc(const moe_desc *d)
+{
+    if (!d)
+        return fail(MOE_ERR_ARG, "desc is NULL");
+    if (d->T < 0)
+        return fail(MOE_ERR_ARG, "T must be >= 0 (got %lld)", (long long)d->T);
+    if (d->k < 1 || d->k > moe::kMaxK)
+        return fail(MOE_ERR_ARG, "k must be in [1, %d] (got %d)", moe::kMaxK, d->k);
+    if (d->E < 1)
+        return fail(MOE_ERR_ARG, "E must be >= 1 (got %d)", d->E);
+    if (d->pad_multiple < 1)
+        return fail(MOE_ERR_ARG, "pad_multiple must be >= 1 (got %d)", d->pad_multiple);
+    if (d->local_begin < 0 || d->num_local < 1 ||
+        static_cast<int64_t>(d->local_begin) + d->num_local > d->E)
+        return fail(MOE_ERR_ARG, "local experts [%d, %d+%d) must lie inside [0, E=%d) and be non-empty",
+                    d->local_begin, d->local_begin, d->num_local, d->E);
+    if (d->num_local > moe::kMaxLocal)
+        return fail(MOE_ERR_ARG, "num_local must be <= %d (got %d)", moe::kMaxLocal, d->num_local);
+    if (d->mode != MOE_EAGER && d->mode != MOE_SYNC_FREE)
+        return fail(MOE_ERR_ARG, "mode must be MOE_EAGER (0) or MOE_SYNC_FREE (1) (got %d)", d->mode);
+    if (d->idx_is_i64 != 0 && d->idx_is_i64 != 1)
+        return fail(MOE_ERR_ARG, "idx_is_i64 must be 0 or 1 (got %d)", d->idx_is_i64);
+    if (d->reserved != 0)
+        return fail(MOE_ERR_ARG, "reserved must be 0");
+    if (d->T * d->k > kI32Max || cap_min(d) > kI32Max)
+        return fail(MOE_ERR_ARG, "T*k and the worst-case row count must fit in int32");
+    if (d->mode == MOE_SYNC_FREE) {
+        if (d->capacity < cap_min(d))
+            return fail(MOE_ERR_CAPACITY,
+                        "sync-free capacity %lld is below the worst case T*min(k,EL) + EL*(P-1) = %lld",
+                        (long long)d->capacity, (long long)cap_min(d));
+        if (d->capacity > kI32Max)
+            return fail(MOE_ERR_ARG, "capacity must fit in int32");
+    }
+    return MOE_OK;
+}
+
+int check_handle(const moe_desc *d, const moe_handle *h)
+{
+    if (!h)
+        return fail(MOE_ERR_ARG, "handle is NULL");
+    if (!h->tokens_per_expert || !h->padded_offsets || !h->status)
+        return fail(MOE_ERR_ARG, "handle tensors tokens_per_expert, padded_offsets and status must be "
+                                 "non-NULL");
+    if (d->T > 0 && !h->row_of_slot)
+        return fail(MOE_ERR_ARG, "handle.row_of_slot must be non-NULL when T > 0");
+    return MOE_OK;
+}
+
+int check_hidden(int32_t H)
+{
+    if (H <= 0 || H % 256 != 0)
+        return fail(MOE_ERR_HIDDEN, "hidden size H must be a positive multiple of 256 (got %d)", H);
+    return MOE_OK;
+}
+
+int check_rows(const moe_desc *d, int64_t R)
+{
+    if (d->mode == MOE_SYNC_FREE) {
+        if (R != d->capacity)
+            return fail(MOE_ERR_ARG, "sync-free mode: R must equal desc->capacity (%lld), got %lld",
+                        (long long)d->capacity, (long long)R);
+    } else if (R < 0 || R > kI32Max) {
+        return fail(MOE_ERR_ARG, "R must be in [0, 2^31) (got %lld)", (long long)R);
+    }
+    return MOE_OK;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct WsLayout {
+    size_t counts_off, flags_off, bytes;
+};
+
+WsLayout ws_layout(const moe_desc *d)
+{
+    const moe::RouteGeom g = moe::route_geom(d->T, d->k, d->num_local);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    WsLayout w;
+    w.counts_off = 0;
+    w.flags_off = up(static_cast<size_t>(g.nblk) * d->num_local * sizeof(int32_t));
+    w.bytes = w.flags_off + up(static_cast<size_t>(g.nblk) * sizeof(int32_t));
+    if (w.bytes == 0)
+        w.bytes = 256;
+    return w;
+}
+
+// Sentinel-fill workgroups: sync-free mode sizes them for the whole worst-case
+// tail; eager mode keeps a handful for the (normally empty) [total, R).
+int64_t sentinel_blocks(const moe_desc *d, int64_t R, int32_t H)
+{
+    if (R <= 0)
+        return d->mode == MOE_EAGER ? 1 : 0;
+    if (d->mode == MOE_EAGER)
+        return 8;
+    const int64_t chunks = R * (H / 8);
+    const int64_t per_block = static_cast<int64_t>(moe::kRowThreads) * 16; // 16 stores per thread
+    int64_t nb = (chunks + per_block - 1) / per_block;
+    if (nb > 4096)
+        nb = 4096;
+    return nb < 1 ? 1 : nb;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity_min(const moe_desc *desc)
+{
+    if (!desc)
+        return -1;
+    return cap_min(desc);
+}
+
+size_t moe_route_workspace_size(const moe_desc *desc)
+{
+    if (check_desc(desc) != MOE_OK)
+        return 0;
+    return ws_layout(desc).bytes;
+}
+
+int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                    float *multihot_probs, const moe_handle *handle, void *workspace,
+                    size_t workspace_bytes, int32_t *host_status, void *stream)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if (desc->T > 0 && !topk_idx)
+        return fail(MOE_ERR_ARG, "topk_idx is NULL");
+    if (multihot_probs && !topk_w)
+        return fail(MOE_ERR_ARG, "multihot_probs requested without topk_w");
+    if (topk_w && !multihot_probs)
+        return fail(MOE_ERR_ARG, "topk_w given but multihot_probs is NULL: route_build only reads "
+                                 "weights to write multihot_probs (pass weights to moe_dispatch)");
+    if (desc->mode == MOE_EAGER && !host_status)
+        return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
+    const WsLayout wl = ws_layout(desc);
+    if (!workspace || workspace_bytes < wl.bytes)
+        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", wl.bytes,
+                    workspace_bytes, workspace ? "" : ", NULL");
+
+    const moe::RouteGeom g = moe::route_geom(desc->T, desc->k, desc->num_local);
+    moe::RouteArgs a;
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.probs = multihot_probs;
+    a.map = handle->routing_map;
+    a.row_of_slot = handle->row_of_slot;
+    a.counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + wl.counts_off);
+    a.blockflags = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + wl.flags_off);
+    a.tpe = handle->tokens_per_expert;
+    a.off = handle->padded_offsets;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.k = desc->k;
+    a.E = desc->E;
+    a.lb = desc->local_begin;
+    a.EL = desc->num_local;
+    a.P = desc->pad_multiple;
+    a.tokens_per_block = g.tokens_per_block;
+    a.nblk = g.nblk;
+    a.idx_i64 = desc->idx_is_i64;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = moe::launch_route(a, g.threads, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "route launch");
+    if (desc->mode == MOE_EAGER) {
+        // "Eager vs captured": the counts come back to the host once.
+        if ((e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s)) != hipSuccess)
+            return hip_fail(e, "status readback");
+        if ((e = hipStreamSynchronize(s)) != hipSuccess)
+            return hip_fail(e, "stream sync");
+        if (host_status[1] & MOE_FLAG_BAD_ID)
+            return fail(MOE_ERR_INDEX, "an expert id outside [-1, E=%d) was seen; such slots were "
+                                       "treated as empty", desc->E);
+    }
+    return ok();
+}
+
+int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                 const float *topk_w, int64_t R, uint16_t *rows, float *row_w, int32_t *row_token,
+                 int32_t *row_expert, void *stream)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if ((rc = check_rows(desc, R)) != MOE_OK)
+        return rc;
+    if (desc->T > 0 && (!x || !aligned16(x)))
+        return fail(MOE_ERR_ARG, "x must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
+    if (R > 0 && (!rows || !aligned16(rows)))
+        return fail(MOE_ERR_ARG, "rows must be a non-NULL, 16-byte aligned [R,H] bf16 tensor");
+    if (row_w && !topk_w && desc->T > 0)
+        return fail(MOE_ERR_ARG, "row_w requested without topk_w");
+    if (topk_w && !row_w)
+        return fail(MOE_ERR_ARG, "topk_w given but row_w is NULL (the weights would be ignored)");
+
+    moe::RowArgs a;
+    a.src = x;
+    a.topk_w = topk_w;
+    a.F = nullptr;
+    a.rows = rows;
+    a.row_w = row_w;
+    a.row_token = row_token;
+    a.row_expert = row_expert;
+    a.dw = nullptr;
+    a.row_of_slot = handle->row_of_slot;
+    a.tpe = handle->tokens_per_expert;
+    a.off = handle->padded_offsets;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.R = R;
+    a.k = desc->k;
+    a.EL = desc->num_local;
+    a.H = H;
+    a.eager = desc->mode == MOE_EAGER;
+    a.ntok_blocks = (desc->T + moe::kRowWaves - 1) / moe::kRowWaves;
+    a.nexp_blocks = R > 0 ? desc->num_local : 0;
+    a.nsent_blocks = sentinel_blocks(desc, R, H);
+    hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "dispatch launch");
+    return ok();
+}
+
+int moe_combine(const moe_desc *desc, const moe_handle *handle, const uint16_t *Y, int32_t H,
+                int64_t R, void *out, int32_t out_is_f32, void *stream)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if ((rc = check_rows(desc, R)) != MOE_OK)
+        return rc;
+    if (out_is_f32 != 0 && out_is_f32 != 1)
+        return fail(MOE_ERR_ARG, "out_is_f32 must be 0 or 1 (got %d)", out_is_f32);
+    if (R > 0 && (!Y || !aligned16(Y)))
+        return fail(MOE_ERR_ARG, "Y must be a non-NULL, 16-byte aligned [R,H] bf16 tensor");
+    if (desc->T > 0 && (!out || !aligned16(out)))
+        return fail(MOE_ERR_ARG, "out must be a non-NULL, 16-byte aligned [T,H] tensor");
+
+    moe::CombineArgs a;
+    a.Y = Y;
+    a.out = out;
+    a.row_of_slot = handle->row_of_slot;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.R = R;
+    a.k = desc->k;
+    a.H = H;
+    a.out_f32 = out_is_f32;
+    a.eager = desc->mode == MOE_EAGER;
+    hipError_t e = moe::launch_combine(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16_t *grad_out,
+                    const uint16_t *expert_out, int32_t H, int64_t R, uint16_t *grad_rows,
+                    float *dw, void *stream)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if ((rc = check_rows(desc, R)) != MOE_OK)
+        return rc;
+    if (desc->T > 0 && (!grad_out || !aligned16(grad_out)))
+        return fail(MOE_ERR_ARG, "grad_out must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
+    if (R > 0 && (!grad_rows || !aligned16(grad_rows)))
+        return fail(MOE_ERR_ARG, "grad_rows must be a non-NULL, 16-byte aligned [R,H] bf16 tensor");
+    if (expert_out && !dw)
+        return fail(MOE_ERR_ARG, "expert_out given but dw is NULL (expert_out is only read for dw)");
+    if (dw && !expert_out && R > 0)
+        return fail(MOE_ERR_ARG, "dw requested without expert_out");
+    if (expert_out && R > 0 && !aligned16(expert_out))
+        return fail(MOE_ERR_ARG, "expert_out must be 16-byte aligned");
+
+    moe::RowArgs a;
+    a.src = grad_out;
+    a.topk_w = nullptr;
+    a.F = expert_out;
+    a.rows = grad_rows;
+    a.row_w = nullptr;
+    a.row_token = nullptr;
+    a.row_expert = nullptr;
+    a.dw = dw;
+    a.row_of_slot = handle->row_of_slot;
+    a.tpe = handle->tokens_per_expert;
+    a.off = handle->padded_offsets;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.R = R;
+    a.k = desc->k;
+    a.EL = desc->num_local;
+    a.H = H;
+    a.eager = desc->mode == MOE_EAGER;
+    a.ntok_blocks = (desc->T + moe::kRowWaves - 1) / moe::kRowWaves;
+    a.nexp_blocks = R > 0 ? desc->num_local : 0;
+    a.nsent_blocks = sentinel_blocks(desc, R, H);
+    hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "combine_bwd launch");
+    return ok();
+}
+
+const char *moe_last_error(void) { return g_err; }
+
+int moe_device_check(int device)
+{
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= n)
+        return fail(MOE_ERR_DEVICE, "device %d not present (%d HIP devices)", device, n);
+    hipDeviceProp_t p;
+    if ((e = hipGetDeviceProperties(&p, device)) != hipSuccess)
+        return hip_fail(e, "hipGetDeviceProperties");
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(MOE_ERR_DEVICE, "device %d is %s; this library is built for gfx950 (MI355X) only",
+                    device, p.gcnArchName);
+    return ok();
+}
+
+}  // extern "C"

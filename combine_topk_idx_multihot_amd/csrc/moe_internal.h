@@ -1,0 +1,82 @@
+// moe_internal.h -- private declarations shared by the HIP sources of libmoe_mi355x.
+// Not installed; the public interface is include/moe_mi355x.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 64;         // slots per token handled lane-parallel by one wave
+constexpr int kMaxLocal = 1024;   // local experts (LDS histogram bound)
+constexpr int kRowWaves = 4;      // waves per workgroup in the row kernels
+constexpr int kRowThreads = kRowWaves * kWave;
+
+// Launch geometry of the routing-count kernel: one workgroup covers
+// tokens_per_block whole tokens (k slots each, one thread per slot).
+struct RouteGeom {
+    int threads;          // 1024, or 512 when EL > 512 (LDS histogram size)
+    int tokens_per_block; // threads / k
+    int64_t nblk;         // ceil(T / tokens_per_block)
+};
+RouteGeom route_geom(int64_t T, int k, int EL);
+
+struct RouteArgs {
+    const void *idx;       // [T,k] int32 or int64
+    const float *w;        // [T,k] or null
+    float *probs;          // [T,E] or null
+    uint8_t *map;          // [T,E] or null
+    int32_t *row_of_slot;  // [T,k]
+    int32_t *counts;       // workspace [nblk][EL]
+    int32_t *blockflags;   // workspace [nblk]
+    int32_t *tpe;          // [EL]
+    int32_t *off;          // [EL+1]
+    int32_t *status;       // [4]
+    int64_t T;
+    int32_t k, E, lb, EL, P;
+    int32_t tokens_per_block;
+    int64_t nblk;
+    int32_t idx_i64;
+};
+
+// K1 histogram + multihot map + in-block ranks; K2 scans; K3 final rows.
+hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s);
+
+struct RowArgs {
+    const uint16_t *src;       // [T,H] token rows (x or grad_out)
+    const float *topk_w;       // [T,k] or null
+    const uint16_t *F;         // [R,H] expert outputs for dw, or null
+    uint16_t *rows;            // [R,H]
+    float *row_w;              // [R] or null
+    int32_t *row_token;        // [R] or null
+    int32_t *row_expert;       // [R] or null
+    float *dw;                 // [T,k] or null
+    const int32_t *row_of_slot;
+    const int32_t *tpe;
+    const int32_t *off;
+    int32_t *status;
+    int64_t T, R;
+    int32_t k, EL, H;
+    int32_t eager;
+    int64_t ntok_blocks, nexp_blocks, nsent_blocks;
+};
+
+// Token-major row movement: dispatch (x -> rows) and the combine backward
+// (grad_out -> grad rows, optional dw); plus pad / sentinel fill.
+hipError_t launch_move_rows(const RowArgs &a, hipStream_t s);
+
+struct CombineArgs {
+    const uint16_t *Y;          // [R,H]
+    void *out;                  // [T,H] bf16 or f32
+    const int32_t *row_of_slot; // [T,k]
+    int32_t *status;
+    int64_t T, R;
+    int32_t k, H;
+    int32_t out_f32;
+    int32_t eager;
+};
+
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+}  // namespace moe

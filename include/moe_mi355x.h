@@ -1,0 +1,192 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) MoE dispatch / combine library.
+ *
+ * One GPU's share of expert-parallel token dispatch and combine in the
+ * "expanded layout": one row per (token, local expert) slot, rows grouped by
+ * local expert, each row carrying that slot's routing weight; the combine sums
+ * rows back to token order.  Sources:
+ *   - "Add the deepep expert-parallel implementation" (huggingface/transformers
+ *     pull request 49638), section "What this adds": bullets "Expanded layout",
+ *     "Eager vs captured", "Custom ops", "Training", "Buffers", and the
+ *     requirements paragraph (hidden size a multiple of 256);
+ *   - "feat: add hybridep" (NVIDIA-NeMo/Automodel pull request 1333): Changelog
+ *     (top-k indices converted to multihot routing metadata) and the reviewed
+ *     HybridEP dispatch call (routing_map, fp32 probs, num_local_experts,
+ *     pad_multiple in; dispatched rows, dispatched probs, tokens_per_expert and
+ *     a handle out).
+ *
+ * Conventions for every entry point
+ *   - All tensors are caller-allocated; the library never allocates device
+ *     memory and keeps no state between calls.  "device" pointers are HIP
+ *     device (or managed) memory on the current device; "host" pointers are
+ *     host memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every launch goes on that stream.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, and every
+ *     row pointer must be 16-byte aligned.
+ *   - Return value is a moe_status; on failure moe_last_error() names the
+ *     violated requirement.  Argument errors are detected on the host before
+ *     anything is launched.  Nothing throws.
+ *   - Only MOE_EAGER moe_route_build synchronizes (once, to read the row
+ *     count back: "Eager vs captured").  Every other call, and every call in
+ *     MOE_SYNC_FREE mode, is asynchronous, allocation-free and safe to record
+ *     into a HIP graph ("Custom ops", "Buffers").
+ *   - Calls that share output buffers must not overlap; calls on different
+ *     buffers may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_ARG = 1,       /* bad sizes, null or misaligned pointers, bad flags */
+    MOE_ERR_HIDDEN = 2,    /* H <= 0 or H % 256 != 0 (requirements paragraph) */
+    MOE_ERR_CAPACITY = 3,  /* sync-free capacity below the worst case */
+    MOE_ERR_WORKSPACE = 4, /* workspace null or smaller than moe_route_workspace_size */
+    MOE_ERR_INDEX = 5,     /* eager: an expert id outside [-1, E) was seen (and dropped) */
+    MOE_ERR_HIP = 6,       /* a HIP runtime call failed */
+    MOE_ERR_DEVICE = 7     /* no usable gfx950 device */
+} moe_status;
+
+typedef enum moe_mode {
+    /* Row count read back to the host; the caller sizes rows to exactly
+     * `total` ("Eager vs captured", eager half). */
+    MOE_EAGER = 0,
+    /* No host sync: rows sized for the worst case (`capacity`); rows past the
+     * device-side total are zero and belong to the sentinel expert
+     * `num_local` ("Eager vs captured", captured half). */
+    MOE_SYNC_FREE = 1
+} moe_mode;
+
+/* Bits of handle.status[1]. */
+enum {
+    MOE_FLAG_BAD_ID = 1,      /* an id outside [-1, E); the slot was treated as -1 */
+    MOE_FLAG_DUPLICATE = 2,   /* a token named the same expert twice; the slots were merged */
+    MOE_FLAG_ROWS_MISMATCH = 4 /* eager: R passed to dispatch/combine != device total */
+};
+
+/* Problem description, shared by every call of one layer. */
+typedef struct moe_desc {
+    int64_t T;            /* tokens (>= 0) */
+    int32_t k;            /* slots per token, 1..64 (top-k) */
+    int32_t E;            /* global experts (>= 1) */
+    int32_t local_begin;  /* first local expert lb */
+    int32_t num_local;    /* local experts EL, 1..1024, lb + EL <= E */
+    int32_t pad_multiple; /* P >= 1: each expert's row group is padded to a multiple of P */
+    int32_t mode;         /* moe_mode */
+    int32_t idx_is_i64;   /* 0: topk_idx is int32 [T,k]; 1: int64 [T,k] */
+    int32_t reserved;     /* must be 0 */
+    int64_t capacity;     /* MOE_SYNC_FREE: rows C >= T*min(k,EL) + EL*(P-1); else ignored */
+} moe_desc;
+
+/* The dispatch handle: plain device tensors, so it can travel through an op
+ * boundary as tensors and be rebuilt ("Custom ops").  Caller-owned. */
+typedef struct moe_handle {
+    uint8_t *routing_map;       /* [T,E] u8 multihot map, or NULL to skip writing it */
+    int32_t *tokens_per_expert; /* [EL] exact (unpadded) routes per local expert */
+    int32_t *padded_offsets;    /* [EL+1] first row of each expert's group; [EL] = total */
+    int32_t *row_of_slot;       /* [T,k] row of each slot, -1 if invalid or not local;
+                                   repeated ids point at the first slot's row */
+    int32_t *status;            /* [4] {total, flags (MOE_FLAG_*), data rows, 0} */
+} moe_handle;
+
+/* Smallest legal sync-free capacity: T*min(k,EL) + EL*(P-1) (worst case: every
+ * token routes all of its slots locally and every group needs P-1 pad rows). */
+int64_t moe_capacity_min(const moe_desc *desc);
+
+/* Device bytes moe_route_build needs as scratch (per-block counts). */
+size_t moe_route_workspace_size(const moe_desc *desc);
+
+/*
+ * Routing preprocessing: top-k ids -> multihot map, tokens_per_expert, padded
+ * offsets and the row of every slot ("feat: add hybridep", Changelog: top-k
+ * indices to multihot routing metadata; dispatch hunk: tokens_per_expert,
+ * pad_multiple).
+ *   topk_idx        device [T,k] int32 or int64 (desc->idx_is_i64); -1 = empty
+ *                   slot; any other id outside [-1, E) is dropped and flagged.
+ *   topk_w          device [T,k] fp32 or NULL; needed only for multihot_probs.
+ *   multihot_probs  device [T,E] fp32 or NULL: the routed weight at each routed
+ *                   expert (repeated ids summed in slot order), 0 elsewhere.
+ *   handle          outputs (see moe_handle); status is fully rewritten.
+ *   workspace       device scratch of >= moe_route_workspace_size bytes.
+ *   host_status     host int32[4]: MOE_EAGER receives {total, flags, data rows, 0}
+ *                   after the one stream sync (pinned memory makes the copy a
+ *                   plain DMA); MOE_SYNC_FREE: unused, may be NULL.
+ * Rows inside an expert's group are in ascending token order.  Returns
+ * MOE_ERR_INDEX in eager mode when MOE_FLAG_BAD_ID is set (outputs valid).
+ */
+int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                    float *multihot_probs, const moe_handle *handle, void *workspace,
+                    size_t workspace_bytes, int32_t *host_status, void *stream);
+
+/*
+ * Dispatch into the expanded layout ("Expanded layout"; "Eager vs captured").
+ *   x           device [T,H] bf16 token rows.
+ *   H           hidden size, a positive multiple of 256.
+ *   topk_w      device [T,k] fp32 routing weights, or NULL (then row_w must be NULL).
+ *   R           rows: MOE_EAGER = host total from moe_route_build;
+ *               MOE_SYNC_FREE = desc->capacity.
+ *   rows        device [R,H] bf16 out: row r = x[row_token[r]] bit for bit; pad
+ *               rows and rows >= total are zero.
+ *   row_w       device [R] fp32 out (the dispatched probs) or NULL: the slot's
+ *               weight (repeated ids summed), 0 on pad and sentinel rows.
+ *   row_token   device [R] int32 out or NULL: source token, -1 on pad/sentinel.
+ *   row_expert  device [R] int32 out or NULL: local expert of the row; pad rows
+ *               carry their group's expert, rows >= total the sentinel num_local.
+ * Writes never go past R.  In eager mode a device total != R sets
+ * MOE_FLAG_ROWS_MISMATCH (and rows in [total, R) are written as sentinel rows).
+ */
+int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                 const float *topk_w, int64_t R, uint16_t *rows, float *row_w,
+                 int32_t *row_token, int32_t *row_expert, void *stream);
+
+/*
+ * Combine: out[t] = sum of Y[row] over t's distinct local slots, in ascending
+ * slot order, in fp32 (the accumulator starts from the first term); no
+ * weights are applied, the experts apply them ("Expanded layout": the
+ * combine only sums).  A token with no local slot gets +0.
+ *   Y           device [R,H] bf16 expert outputs.
+ *   out         device [T,H]: bf16 rounded to nearest-even (NaN -> 0x7FC0) when
+ *               out_is_f32 == 0, fp32 when out_is_f32 == 1.
+ */
+int moe_combine(const moe_desc *desc, const moe_handle *handle, const uint16_t *Y, int32_t H,
+                int64_t R, void *out, int32_t out_is_f32, void *stream);
+
+/*
+ * Combine backward = a cached dispatch of grad_out along the forward's rows
+ * ("Custom ops": the combine's backward is a cached dispatch), plus the
+ * routing-weight gradients ("Training").
+ *   grad_out    device [T,H] bf16.
+ *   expert_out  device [R,H] bf16 expert outputs before the routing weight is
+ *               applied, or NULL (then dw must be NULL).
+ *   grad_rows   device [R,H] bf16 out: grad_out[row_token[r]]; pad and
+ *               sentinel rows zero.
+ *   dw          device [T,k] fp32 out or NULL: dot(grad_out[t], expert_out[row
+ *               of slot (t,j)]) with exact products and an fp64 sum, rounded
+ *               once to fp32; repeated ids share the value; 0 for slots that
+ *               are empty or not local.
+ */
+int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16_t *grad_out,
+                    const uint16_t *expert_out, int32_t H, int64_t R, uint16_t *grad_rows,
+                    float *dw, void *stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *moe_last_error(void);
+
+/* MOE_OK if `device` is a gfx950 GPU the library can run on; otherwise
+ * MOE_ERR_DEVICE (or MOE_ERR_HIP) with the reason in moe_last_error().
+ * Does not launch anything. */
+int moe_device_check(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,178 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented codes before touching the GPU.
+
+No kernel is launched here: every call below fails host validation, which runs
+before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from combine_topk_idx_multihot_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_mi355x.h")
+FAKE = 0x100000  # a 16-byte aligned non-NULL address; never dereferenced by validation
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_desc_struct_layout_matches_header():
+    assert ctypes.sizeof(B.Desc) == 48
+    assert B.Desc.capacity.offset == 40
+    assert ctypes.sizeof(B._Handle) == 5 * 8
+
+
+def _desc(**kw):
+    base = dict(T=100, k=8, E=128, local_begin=0, num_local=128, pad_multiple=16,
+                mode=B.MOE_EAGER, idx_is_i64=False, capacity=0)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+def _handle():
+    h = B._Handle(routing_map=FAKE, tokens_per_expert=FAKE, padded_offsets=FAKE,
+                  row_of_slot=FAKE, status=FAKE)
+    return h
+
+
+def route_rc(d, ws_bytes=1 << 20, idx=FAKE, w=None, probs=None, host=FAKE, handle=None):
+    h = handle if handle is not None else _handle()
+    return B.lib().moe_route_build(ctypes.byref(d), idx, w, probs, ctypes.byref(h), FAKE, ws_bytes,
+                                   host, None)
+
+
+def dispatch_rc(d, H=2048, R=10, x=FAKE, rows=FAKE, w=None, row_w=None):
+    h = _handle()
+    return B.lib().moe_dispatch(ctypes.byref(d), ctypes.byref(h), x, H, w, R, rows, row_w, None,
+                                None, None)
+
+
+def combine_rc(d, H=2048, R=10, Y=FAKE, out=FAKE, f32=0):
+    h = _handle()
+    return B.lib().moe_combine(ctypes.byref(d), ctypes.byref(h), Y, H, R, out, f32, None)
+
+
+def bwd_rc(d, H=2048, R=10, g=FAKE, F=None, gr=FAKE, dw=None):
+    h = _handle()
+    return B.lib().moe_combine_bwd(ctypes.byref(d), ctypes.byref(h), g, F, H, R, gr, dw, None)
+
+
+@pytest.mark.parametrize("H", [0, -256, 100, 384, 2049])
+def test_hidden_must_be_multiple_of_256(H):
+    d = _desc()
+    for rc in (dispatch_rc(d, H=H), combine_rc(d, H=H), bwd_rc(d, H=H)):
+        assert rc == B.MOE_ERR_HIDDEN
+    assert "256" in B.last_error()
+
+
+@pytest.mark.parametrize("field,value", [
+    ("T", -1), ("k", 0), ("k", 65), ("E", 0), ("pad_multiple", 0), ("local_begin", -1),
+    ("num_local", 0), ("num_local", 129), ("mode", 2), ("num_local", 1025),
+])
+def test_bad_desc_is_rejected(field, value):
+    kw = {field: value}
+    if field == "num_local" and value == 1025:
+        kw["E"] = 2048
+    d = _desc(**kw)
+    assert route_rc(d) == B.MOE_ERR_ARG
+    assert dispatch_rc(d) == B.MOE_ERR_ARG
+    assert B.last_error()
+
+
+def test_local_range_must_fit():
+    assert route_rc(_desc(local_begin=120, num_local=16)) == B.MOE_ERR_ARG
+
+
+def test_sync_free_capacity_rule():
+    T, k, EL, P = 100, 8, 16, 4
+    cmin = T * min(k, EL) + EL * (P - 1)
+    d = _desc(T=T, k=k, num_local=EL, pad_multiple=P, mode=B.MOE_SYNC_FREE, capacity=cmin - 1)
+    assert B.moe_capacity_min(d) == cmin == oracle.capacity_min(T, k, EL, P)
+    assert route_rc(d) == B.MOE_ERR_CAPACITY
+    assert "worst case" in B.last_error()
+    d.capacity = cmin
+    # sync-free rows must equal the capacity
+    assert dispatch_rc(d, R=cmin - 1) == B.MOE_ERR_ARG
+
+
+def test_capacity_min_matches_oracle_on_a_grid():
+    for T in (0, 1, 7, 4096):
+        for k in (1, 2, 8):
+            for EL in (1, 4, 16, 128):
+                for P in (1, 2, 16, 128):
+                    d = _desc(T=T, k=k, num_local=EL, pad_multiple=P)
+                    assert B.moe_capacity_min(d) == oracle.capacity_min(T, k, EL, P)
+
+
+def test_workspace_rules():
+    d = _desc()
+    need = B.moe_route_workspace_size(d)
+    assert need > 0
+    assert route_rc(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+    assert B.lib().moe_route_workspace_size(ctypes.byref(_desc(k=0))) == 0
+
+
+def test_route_flag_pairs_are_never_ignored():
+    d = _desc()
+    assert route_rc(d, w=FAKE, probs=None) == B.MOE_ERR_ARG       # weights with nothing to write
+    assert route_rc(d, w=None, probs=FAKE) == B.MOE_ERR_ARG       # probs without weights
+    assert route_rc(d, host=None) == B.MOE_ERR_ARG                # eager needs the host status
+    h = _handle()
+    h.row_of_slot = None
+    assert route_rc(d, handle=h) == B.MOE_ERR_ARG
+    assert route_rc(d, idx=None) == B.MOE_ERR_ARG
+
+
+def test_dispatch_pointer_rules():
+    d = _desc()
+    assert dispatch_rc(d, x=None) == B.MOE_ERR_ARG
+    assert dispatch_rc(d, x=FAKE + 8) == B.MOE_ERR_ARG  # not 16-byte aligned
+    assert dispatch_rc(d, rows=FAKE + 2) == B.MOE_ERR_ARG
+    assert dispatch_rc(d, w=FAKE, row_w=None) == B.MOE_ERR_ARG
+    assert dispatch_rc(d, w=None, row_w=FAKE) == B.MOE_ERR_ARG
+    assert dispatch_rc(d, R=-1) == B.MOE_ERR_ARG
+
+
+def test_combine_and_bwd_pointer_rules():
+    d = _desc()
+    assert combine_rc(d, f32=2) == B.MOE_ERR_ARG
+    assert combine_rc(d, Y=None) == B.MOE_ERR_ARG
+    assert combine_rc(d, out=FAKE + 4) == B.MOE_ERR_ARG
+    assert bwd_rc(d, F=FAKE, dw=None) == B.MOE_ERR_ARG
+    assert bwd_rc(d, F=None, dw=FAKE) == B.MOE_ERR_ARG
+    assert bwd_rc(d, g=None) == B.MOE_ERR_ARG
+
+
+def test_validation_agrees_with_oracle_argument_rules():
+    cases = [
+        dict(T=10, k=2, E=8, local_begin=0, num_local=8, pad_multiple=1),
+        dict(T=10, k=2, E=8, local_begin=4, num_local=5, pad_multiple=1),
+        dict(T=10, k=2, E=8, local_begin=0, num_local=8, pad_multiple=0),
+        dict(T=-1, k=2, E=8, local_begin=0, num_local=8, pad_multiple=1),
+        dict(T=10, k=0, E=8, local_begin=0, num_local=8, pad_multiple=1),
+    ]
+    for c in cases:
+        want = oracle.check_args(c["T"], c["k"], c["E"], c["local_begin"], c["num_local"],
+                                 c["pad_multiple"])
+        d = _desc(**c)
+        if want == oracle.OK:
+            # valid: only the (launch-free) workspace query is called
+            assert B.lib().moe_route_workspace_size(ctypes.byref(d)) > 0
+        else:
+            assert route_rc(d, ws_bytes=1 << 30) == want
