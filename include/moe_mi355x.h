@@ -149,9 +149,10 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
 
 /*
  * Combine: out[t] = sum of Y[row] over t's distinct local slots, in ascending
- * slot order, in fp32 (the accumulator starts from the first term); no
- * weights are applied, the experts apply them ("Expanded layout": the
- * combine only sums).  A token with no local slot gets +0.
+ * slot order, in fp32 (the accumulator starts from the first term).  No
+ * weight is applied here: in the expanded layout the experts weight their
+ * own rows and the combine is a plain sum ("Expanded layout").  A token with
+ * no local slot gets +0.
  *   Y           device [R,H] bf16 expert outputs.
  *   out         device [T,H]: bf16 rounded to nearest-even (NaN -> 0x7FC0) when
  *               out_is_f32 == 0, fp32 when out_is_f32 == 1.

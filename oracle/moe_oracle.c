@@ -273,7 +273,7 @@ static int primary_local(const int64_t *idx, int64_t t, int32_t j, int32_t k, in
 }
 
 /* ------------------------------------------------------------------------- */
-/* Combine ([DEP] "Expanded layout": the combine only sums).                 */
+/* Combine ([DEP] "Expanded layout": a plain sum, weights belong to experts) */
 /* ------------------------------------------------------------------------- */
 
 /* out[t] = sum over the primary local slots of t, ascending slot order, of
