@@ -10,8 +10,10 @@ implementation": distinct layers back to back, median of windows):
   * `--sets` (default 4) independent layer buffer sets, each with its own
     routing, rotated step by step so a step's inputs were last touched several
     hundred MB of traffic earlier (MI355X's 256 MB Infinity Cache);
-  * combine reads a separate expert-output buffer (a stand-in for the grouped
-    GEMM output), which also serves as the expert output of the backward;
+  * combine reads its own expert-output buffer Y (a stand-in for the grouped
+    GEMM output) and the backward reads another one, F (the expert output
+    before the routing weight), so no kernel of a step re-reads what an
+    earlier kernel of the same step left in cache;
   * W warm-up steps, then K timed steps between two device synchronizations;
     each kernel is also bracketed by HIP events on the launch stream.
 
@@ -64,7 +66,13 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall budget of the oracle CPU-baseline leg (0 = skip)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 8 plain device-to-device copies of MIB MiB (torch copy_) and "
+                         "exit: the reference kernel for scaling HBM traffic counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share only (no inter-GPU exchange is built); "
@@ -99,6 +107,7 @@ def main():
             "x": torch.randn((wl.T, H), generator=gen, device=dev).to(torch.bfloat16),
             "g": torch.randn((wl.T, H), generator=gen, device=dev).to(torch.bfloat16),
             "Y": torch.randn((Rmax, H), generator=gen, device=dev).to(torch.bfloat16),
+            "F": torch.randn((Rmax, H), generator=gen, device=dev).to(torch.bfloat16),
             "rows": torch.empty((Rmax, H), dtype=torch.bfloat16, device=dev),
             "grad_rows": torch.empty((Rmax, H), dtype=torch.bfloat16, device=dev),
             "row_w": torch.empty(Rmax, dtype=torch.float32, device=dev),
@@ -108,7 +117,6 @@ def main():
             "dw": torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev),
             "probs": torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev),
             "h": B.alloc_handle(d, dev),
-            "ws": B.workspace_for(d, dev),
         }
         sets.append(st)
     torch.cuda.synchronize()
@@ -119,7 +127,7 @@ def main():
         ev = events
         if ev is not None:
             ev[0].record(stream)
-        B.moe_route_build(d, st["idx"], st["h"], st["ws"], st["w"], st["probs"], stream=stream)
+        B.moe_route_build(d, st["idx"], st["h"], st["w"], st["probs"], stream=stream)
         R = wl.cap if wl.sync_free else st["h"].total
         if ev is not None:
             ev[1].record(stream)
@@ -130,7 +138,7 @@ def main():
         B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)
         if ev is not None:
             ev[3].record(stream)
-        B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["Y"], st["dw"],
+        B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["F"], st["dw"],
                           stream=stream)
         if ev is not None:
             ev[4].record(stream)
@@ -212,6 +220,25 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def calibrate_copy(mib):
+    """Plain copies of a known size: each launch reads and writes `mib` MiB, so
+    a traffic counter's reading for it gives the counter's scale."""
+    import torch
+
+    n = mib * (1 << 20)
+    bufs = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    for b in bufs:
+        b.fill_(1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(8):
+        bufs[(2 * i + 1) % 4].copy_(bufs[(2 * i) % 4])
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 8
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 8, "GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 def cpu_baseline(wl, st, budget_s, torch):
     import oracle
 
@@ -220,14 +247,14 @@ def cpu_baseline(wl, st, budget_s, torch):
     x, g = u16(st["x"]), u16(st["g"])
     EL = wl.num_local
     C = wl.cap if wl.sync_free else 0
-    Y = u16(st["Y"])
+    Y, F = u16(st["Y"]), u16(st["F"])
     reps, t_used, bytes_done = 0, 0.0, 0
     while t_used < budget_s and reps < 50:
         t0 = time.perf_counter()
         r = oracle.route(idx, wl.E, wl.lb, EL, wl.P, sync_free=wl.sync_free, C=C, w=w, x=x,
                          want_probs=True)
         oracle.combine(idx, r.row_of_slot, Y[:r.R], wl.E, wl.lb, EL)
-        oracle.combine_bwd(idx, r.row_of_slot, r.row_token, g, wl.E, wl.lb, EL, F=Y[:r.R], R=r.R)
+        oracle.combine_bwd(idx, r.row_of_slot, r.row_token, g, wl.E, wl.lb, EL, F=F[:r.R], R=r.R)
         t_used += time.perf_counter() - t0
         local = (idx >= wl.lb) & (idx < wl.lb + EL)
         bm = byte_model(wl, int(r.tpe.sum()), r.R, int(local.any(axis=1).sum()), 4, True)

@@ -49,7 +49,8 @@ class Desc(ctypes.Structure):
 class _Handle(ctypes.Structure):
     _fields_ = [("routing_map", ctypes.c_void_p), ("tokens_per_expert", ctypes.c_void_p),
                 ("padded_offsets", ctypes.c_void_p), ("row_of_slot", ctypes.c_void_p),
-                ("status", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -69,7 +70,7 @@ def lib() -> ctypes.CDLL:
         L.moe_capacity_min.restype = i64
         L.moe_route_workspace_size.argtypes = [pd]
         L.moe_route_workspace_size.restype = ctypes.c_size_t
-        L.moe_route_build.argtypes = [pd, vp, vp, vp, ph, vp, ctypes.c_size_t, vp, vp]
+        L.moe_route_build.argtypes = [pd, vp, vp, vp, ph, vp, vp]
         L.moe_route_build.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp]
         L.moe_dispatch.restype = ctypes.c_int
@@ -141,10 +142,13 @@ class Handle:
     row_of_slot: torch.Tensor          # [T,k] int32
     status: torch.Tensor               # [4] int32 (device)
     host_status: torch.Tensor          # [4] int32 (pinned host)
+    workspace: torch.Tensor            # [moe_route_workspace_size] uint8 (device)
 
     def c(self) -> _Handle:
         d = self.desc
         return _Handle(
+            workspace=_dev(self.workspace, "workspace", torch.uint8, moe_route_workspace_size(d)),
+            workspace_bytes=self.workspace.numel(),
             routing_map=_dev(self.routing_map, "routing_map", torch.uint8, d.T * d.E, True),
             tokens_per_expert=_dev(self.tokens_per_expert, "tokens_per_expert", torch.int32,
                                    d.num_local),
@@ -172,7 +176,8 @@ def alloc_handle(desc: Desc, device="cuda", with_map: bool = True) -> Handle:
         padded_offsets=torch.empty(EL + 1, dtype=torch.int32, device=device),
         row_of_slot=torch.empty((T, k), dtype=torch.int32, device=device),
         status=torch.empty(4, dtype=torch.int32, device=device),
-        host_status=torch.zeros(4, dtype=torch.int32, pin_memory=True))
+        host_status=torch.zeros(4, dtype=torch.int32, pin_memory=True),
+        workspace=torch.empty(moe_route_workspace_size(desc), dtype=torch.uint8, device=device))
 
 
 # ---------------------------------------------------------------------------
@@ -190,7 +195,7 @@ def moe_route_workspace_size(desc: Desc) -> int:
     return n
 
 
-def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle, workspace: torch.Tensor,
+def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle,
                     topk_w: torch.Tensor | None = None, multihot_probs: torch.Tensor | None = None,
                     stream=None) -> int:
     """Returns MOE_OK; eager mode fills handle.host_status (total, flags, data rows)."""
@@ -199,14 +204,12 @@ def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle, workspac
     p_idx = _dev(topk_idx, "topk_idx", idx_dtype, n) if n else None
     p_w = _dev(topk_w, "topk_w", torch.float32, n, optional=True)
     p_probs = _dev(multihot_probs, "multihot_probs", torch.float32, desc.T * desc.E, optional=True)
-    p_ws = _dev(workspace, "workspace", torch.uint8, 0)
-    ws_bytes = workspace.numel()
     hs = handle.host_status
     if hs.is_cuda or hs.dtype != torch.int32 or hs.numel() < 4:
         raise MoeError(MOE_ERR_ARG, "host_status must be a host int32 tensor of 4 elements")
     h = handle.c()
     return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, ctypes.byref(h),
-                                        p_ws, ws_bytes, hs.data_ptr(), _stream(stream)))
+                                        hs.data_ptr(), _stream(stream)))
 
 
 def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, rows: torch.Tensor,
@@ -262,20 +265,14 @@ def moe_device_check(device: int = 0) -> int:
 # convenience wrappers that allocate outputs
 # ---------------------------------------------------------------------------
 
-def workspace_for(desc: Desc, device="cuda") -> torch.Tensor:
-    return torch.empty(moe_route_workspace_size(desc), dtype=torch.uint8, device=device)
-
-
 def route(desc: Desc, topk_idx: torch.Tensor, topk_w: torch.Tensor | None = None,
           want_probs: bool = False, with_map: bool = True, handle: Handle | None = None,
-          workspace: torch.Tensor | None = None, stream=None):
+          stream=None):
     """moe_route_build with fresh outputs.  Returns (handle, multihot_probs or None)."""
     dev = topk_idx.device
     handle = handle or alloc_handle(desc, dev, with_map=with_map)
-    workspace = workspace if workspace is not None else workspace_for(desc, dev)
     probs = torch.empty((desc.T, desc.E), dtype=torch.float32, device=dev) if want_probs else None
-    moe_route_build(desc, topk_idx, handle, workspace, topk_w if want_probs else None, probs,
-                    stream=stream)
+    moe_route_build(desc, topk_idx, handle, topk_w if want_probs else None, probs, stream=stream)
     return handle, probs
 
 

@@ -81,10 +81,32 @@ int check_desc(const moe_desc *d)
     return MOE_OK;
 }
 
+struct WsLayout {
+    size_t counts_off, flags_off, bytes;
+};
+
+// The handle's workspace: route scratch, per-block expert counts and flags.
+WsLayout ws_layout(const moe_desc *d)
+{
+    const moe::RouteGeom g = moe::route_geom(d->T, d->k, d->num_local);
+    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    WsLayout w;
+    w.counts_off = 0;
+    w.flags_off = up(static_cast<size_t>(g.nblk) * d->num_local * sizeof(int32_t));
+    w.bytes = w.flags_off + up(static_cast<size_t>(g.nblk) * sizeof(int32_t));
+    if (w.bytes == 0)
+        w.bytes = 256;
+    return w;
+}
+
 int check_handle(const moe_desc *d, const moe_handle *h)
 {
     if (!h)
         return fail(MOE_ERR_ARG, "handle is NULL");
+    const WsLayout wl = ws_layout(d);
+    if (!h->workspace || h->workspace_bytes < wl.bytes)
+        return fail(MOE_ERR_WORKSPACE, "handle.workspace needs %zu bytes (got %zu%s)", wl.bytes,
+                    h->workspace_bytes, h->workspace ? "" : ", NULL");
     if (!h->tokens_per_expert || !h->padded_offsets || !h->status)
         return fail(MOE_ERR_ARG, "handle tensors tokens_per_expert, padded_offsets and status must be "
                                  "non-NULL");
@@ -117,38 +139,7 @@ int hip_fail(hipError_t e, const char *what)
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-struct WsLayout {
-    size_t counts_off, flags_off, bytes;
-};
 
-WsLayout ws_layout(const moe_desc *d)
-{
-    const moe::RouteGeom g = moe::route_geom(d->T, d->k, d->num_local);
-    auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    WsLayout w;
-    w.counts_off = 0;
-    w.flags_off = up(static_cast<size_t>(g.nblk) * d->num_local * sizeof(int32_t));
-    w.bytes = w.flags_off + up(static_cast<size_t>(g.nblk) * sizeof(int32_t));
-    if (w.bytes == 0)
-        w.bytes = 256;
-    return w;
-}
-
-// Sentinel-fill workgroups: sync-free mode sizes them for the whole worst-case
-// tail; eager mode keeps a handful for the (normally empty) [total, R).
-int64_t sentinel_blocks(const moe_desc *d, int64_t R, int32_t H)
-{
-    if (R <= 0)
-        return d->mode == MOE_EAGER ? 1 : 0;
-    if (d->mode == MOE_EAGER)
-        return 8;
-    const int64_t chunks = R * (H / 8);
-    const int64_t per_block = static_cast<int64_t>(moe::kRowThreads) * 16; // 16 stores per thread
-    int64_t nb = (chunks + per_block - 1) / per_block;
-    if (nb > 4096)
-        nb = 4096;
-    return nb < 1 ? 1 : nb;
-}
 
 }  // namespace
 
@@ -169,8 +160,8 @@ size_t moe_route_workspace_size(const moe_desc *desc)
 }
 
 int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                    float *multihot_probs, const moe_handle *handle, void *workspace,
-                    size_t workspace_bytes, int32_t *host_status, void *stream)
+                    float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                    void *stream)
 {
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
@@ -187,9 +178,7 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     if (desc->mode == MOE_EAGER && !host_status)
         return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
     const WsLayout wl = ws_layout(desc);
-    if (!workspace || workspace_bytes < wl.bytes)
-        return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu%s)", wl.bytes,
-                    workspace_bytes, workspace ? "" : ", NULL");
+    char *workspace = static_cast<char *>(handle->workspace);
 
     const moe::RouteGeom g = moe::route_geom(desc->T, desc->k, desc->num_local);
     moe::RouteArgs a;
@@ -198,8 +187,8 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     a.probs = multihot_probs;
     a.map = handle->routing_map;
     a.row_of_slot = handle->row_of_slot;
-    a.counts = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + wl.counts_off);
-    a.blockflags = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + wl.flags_off);
+    a.counts = reinterpret_cast<int32_t *>(workspace + wl.counts_off);
+    a.blockflags = reinterpret_cast<int32_t *>(workspace + wl.flags_off);
     a.tpe = handle->tokens_per_expert;
     a.off = handle->padded_offsets;
     a.status = handle->status;
@@ -212,6 +201,17 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     a.tokens_per_block = g.tokens_per_block;
     a.nblk = g.nblk;
     a.idx_i64 = desc->idx_is_i64;
+    a.host_status = nullptr;
+    if (desc->mode == MOE_EAGER) {
+        // Pinned (device-visible) host memory: the kernel writes the status
+        // there directly; pageable memory takes a copy after the kernels.
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, host_status) == hipSuccess &&
+            attr.type == hipMemoryTypeHost && attr.devicePointer)
+            a.host_status = static_cast<int32_t *>(attr.devicePointer);
+        else
+            (void)hipGetLastError(); // an unregistered pointer is not an error here
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = moe::launch_route(a, g.threads, s);
@@ -219,7 +219,8 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
         return hip_fail(e, "route launch");
     if (desc->mode == MOE_EAGER) {
         // "Eager vs captured": the counts come back to the host once.
-        if ((e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
+        if (!a.host_status &&
+            (e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
                                 hipMemcpyDeviceToHost, s)) != hipSuccess)
             return hip_fail(e, "status readback");
         if ((e = hipStreamSynchronize(s)) != hipSuccess)
@@ -272,9 +273,7 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
     a.EL = desc->num_local;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
-    a.ntok_blocks = (desc->T + moe::kRowWaves - 1) / moe::kRowWaves;
-    a.nexp_blocks = R > 0 ? desc->num_local : 0;
-    a.nsent_blocks = sentinel_blocks(desc, R, H);
+    moe::row_shape(a);
     hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "dispatch launch");
@@ -360,9 +359,7 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     a.EL = desc->num_local;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
-    a.ntok_blocks = (desc->T + moe::kRowWaves - 1) / moe::kRowWaves;
-    a.nexp_blocks = R > 0 ? desc->num_local : 0;
-    a.nsent_blocks = sentinel_blocks(desc, R, H);
+    moe::row_shape(a);
     hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "combine_bwd launch");

@@ -9,14 +9,14 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kMaxK = 64;         // slots per token handled lane-parallel by one wave
-constexpr int kMaxLocal = 1024;   // local experts (LDS histogram bound)
+constexpr int kMaxLocal = 1024;   // local experts (LDS bitmap bound)
 constexpr int kRowWaves = 4;      // waves per workgroup in the row kernels
 constexpr int kRowThreads = kRowWaves * kWave;
 
 // Launch geometry of the routing-count kernel: one workgroup covers
 // tokens_per_block whole tokens (k slots each, one thread per slot).
 struct RouteGeom {
-    int threads;          // 1024, or 512 when EL > 512 (LDS histogram size)
+    int threads;          // 1024, 512 or 256 (the LDS bitmaps hold EL x threads bits)
     int tokens_per_block; // threads / k
     int64_t nblk;         // ceil(T / tokens_per_block)
 };
@@ -33,6 +33,7 @@ struct RouteArgs {
     int32_t *tpe;          // [EL]
     int32_t *off;          // [EL+1]
     int32_t *status;       // [4]
+    int32_t *host_status;  // [4] device-visible alias of the caller's host copy, or null
     int64_t T;
     int32_t k, E, lb, EL, P;
     int32_t tokens_per_block;
@@ -40,7 +41,7 @@ struct RouteArgs {
     int32_t idx_i64;
 };
 
-// K1 histogram + multihot map + in-block ranks; K2 scans; K3 final rows.
+// K1 counts + multihot map + in-block ranks; K2 offsets and final rows.
 hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s);
 
 struct RowArgs {
@@ -59,11 +60,16 @@ struct RowArgs {
     int64_t T, R;
     int32_t k, EL, H;
     int32_t eager;
+    int32_t seg;               // 16-byte chunks per lane per segment
+    int32_t waves_per_token;   // 1, 2 or 4: a token's segments are dealt over these waves
     int64_t ntok_blocks, nexp_blocks, nsent_blocks;
 };
 
-// Token-major row movement: dispatch (x -> rows) and the combine backward
-// (grad_out -> grad rows, optional dw); plus pad / sentinel fill.
+// Row movement: dispatch (x -> rows) and the combine backward (grad_out ->
+// grad rows, optional dw), token-major; plus pad / sentinel fill.
+// row_shape fills in the launch shape (segment size, waves per token, block
+// counts) from the other fields.
+void row_shape(RowArgs &a);
 hipError_t launch_move_rows(const RowArgs &a, hipStream_t s);
 
 struct CombineArgs {

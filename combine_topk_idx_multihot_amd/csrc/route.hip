@@ -7,36 +7,47 @@
 // implementation", "What this adds" / "Expanded layout": one row per (token,
 // local expert) slot, grouped by local expert (here in ascending token order).
 //
-// Three launches, no atomics on the ordering path, so the layout is the same
-// on every run:
-//   K1 route_count  one thread per slot, one workgroup per block of whole
-//                   tokens.  Writes the multihot map (and probs), detects bad
-//                   and repeated ids, and ranks each primary local slot among
-//                   the block's slots of the same expert with wave ballots
-//                   (lanes are in token order, so a ballot prefix popcount is
-//                   a stable rank).  Per-block expert counts go to workspace.
-//   K2 route_scan   one workgroup: per-expert exclusive scan over blocks,
-//                   tokens_per_expert, padded sizes and their exclusive scan
-//                   over experts (= padded offsets), device total, flags.
-//   K3 route_rows   one thread per slot: row = offset[e] + block base[e] +
-//                   in-block rank.
+// The layout is identical on every run: the only atomics are bit-ORs into
+// LDS bitmaps, whose result does not depend on their order.
+//   K1 route_count   one thread per slot, one workgroup per block of whole
+//                    tokens.  The block's ids (and weights) are staged in LDS
+//                    with one coalesced load each.  It zero-fills its rows of
+//                    the multihot map (and probs) and scatters the routed
+//                    entries, detects bad and repeated ids, and sets the bit of
+//                    each primary local slot in its expert's slot bitmap.  A
+//                    slot's in-block rank is then the popcount of its expert's
+//                    bits below it (slots are in token order, so the rank is
+//                    the ascending-token rank).  Per-block expert counts go to
+//                    the workspace; each slot keeps (expert << 11 | in-block
+//                    rank) until the final pass.
+//   K2 route_finish  one workgroup per K1 block: every block reads the whole
+//                    (small) count table, forms its own per-expert base and the
+//                    global totals, scans the padded totals into offsets in LDS
+//                    and rewrites its slots to final rows; block 0 publishes
+//                    tokens_per_expert, offsets and the status word.
+//   Large T (count table > 64 Ki entries) takes a three-launch form instead:
+//   K2s route_scan (one workgroup) then K3 route_rows (one thread per slot).
 #include "moe_internal.h"
 
 namespace moe {
 
+// Between the passes a slot holds (expert << 11) | in-block rank: the rank is
+// < 2048 (workgroups are <= 1024 threads) and the local expert < 1024.
+constexpr int kRankBits = 11;
+constexpr int kExpertBits = 10;
+
+__device__ __forceinline__ int packed_expert(int v) { return (v >> kRankBits) & ((1 << kExpertBits) - 1); }
+__device__ __forceinline__ int packed_rank(int v) { return v & ((1 << kRankBits) - 1); }
+constexpr int64_t kFusedFinishMax = 65536;  // nblk * EL bound for the fused finish
+
 RouteGeom route_geom(int64_t T, int k, int EL)
 {
     RouteGeom g;
-    g.threads = EL > 512 ? 512 : 1024;
+    // LDS bitmaps hold EL x threads bits: keep EL * threads <= 256 Ki
+    g.threads = EL <= 256 ? 1024 : (EL <= 512 ? 512 : 256);
     g.tokens_per_block = g.threads / k;
     g.nblk = T > 0 ? (T + g.tokens_per_block - 1) / g.tokens_per_block : 0;
     return g;
-}
-
-template <typename IT>
-__device__ __forceinline__ int64_t id_at(const IT *__restrict__ p, int64_t i)
-{
-    return static_cast<int64_t>(p[i]);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -45,179 +56,147 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // K1
 // ---------------------------------------------------------------------------
+// LDS of K1: slot bitmaps [EL][W] u32 and their popcount prefixes [EL][W] u16
+// (W = threads/32 words per expert), staged ids and weights, one flag word.
+static size_t count_lds_bytes(int threads, int EL)
+{
+    const size_t words = static_cast<size_t>(EL) * (threads / 32);
+    return words * 4 + ((words + 1) & ~static_cast<size_t>(1)) * 2 +
+           static_cast<size_t>(threads) * 8 + 4;
+}
+
 template <typename IT>
 __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
 {
     extern __shared__ int32_t lds[];
     const int nthreads = blockDim.x;
-    const int nwaves = nthreads / kWave;
+    const int W = nthreads / 32; // bitmap words per expert
     const int EL = a.EL;
-    int32_t *cnt = lds;                    // [nwaves][EL] per-wave counts, then wave bases
-    int32_t *lrank = cnt + nwaves * EL;    // [nthreads] in-block rank of each slot
-    int32_t *bflag = lrank + nthreads;     // block flag word
+    uint32_t *bm = reinterpret_cast<uint32_t *>(lds);          // [EL][W] slots of each expert
+    uint16_t *pref = reinterpret_cast<uint16_t *>(bm + EL * W); // [EL][W] exclusive popcounts
+    int32_t *sid = reinterpret_cast<int32_t *>(pref + ((EL * W + 1) & ~1)); // staged ids
+    float *sw = reinterpret_cast<float *>(sid + nthreads);                   // staged weights
+    int32_t *bflag = reinterpret_cast<int32_t *>(sw + nthreads);
 
     const IT *__restrict__ idx = static_cast<const IT *>(a.idx);
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
     const int64_t b = blockIdx.x;
     const int k = a.k;
     const int64_t t0 = b * a.tokens_per_block;
     const int64_t t1 = min(a.T, t0 + a.tokens_per_block);
+    const int nslots = static_cast<int>((t1 - t0) * k);
+    const int64_t s = t0 * k + tid;
 
-    for (int i = tid; i < nwaves * EL; i += nthreads)
-        cnt[i] = 0;
+    for (int i = tid; i < EL * W; i += nthreads)
+        bm[i] = 0;
+    int myid = -1; // -2 marks an id outside [-1, E)
+    if (tid < nslots) {
+        const int64_t e = static_cast<int64_t>(idx[s]);
+        myid = (e >= -1 && e < a.E) ? static_cast<int>(e) : -2;
+    }
+    sid[tid] = myid;
+    if (a.probs)
+        sw[tid] = tid < nslots ? a.w[s] : 0.f;
     if (tid == 0)
         *bflag = 0;
-
-    // Phase A: this block's rows of the multihot map and of the probs.
+    // Zero this block's rows of the map and the probs (coalesced); the routed
+    // entries are written after the barrier below.
     if (a.map) {
         uint8_t *base = a.map + t0 * a.E;
-        if ((a.E & 15) == 0 && (reinterpret_cast<uintptr_t>(a.map) & 15) == 0) {
-            const int cpt = a.E >> 4; // 16-byte chunks per token row
-            const int64_t nch = (t1 - t0) * cpt;
-            for (int64_t q = tid; q < nch; q += nthreads) {
-                const int64_t t = t0 + q / cpt;
-                const int eb = static_cast<int>(q % cpt) * 16;
-                uint64_t lo = 0, hi = 0;
-                for (int j = 0; j < k; ++j) {
-                    const int64_t d = id_at(idx, t * k + j) - eb;
-                    if (d >= 0 && d < 16) {
-                        const uint64_t bit = 1ull << ((d & 7) * 8);
-                        if (d < 8)
-                            lo |= bit;
-                        else
-                            hi |= bit;
-                    }
-                }
-                u32x4 v = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
-                           static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
-                *reinterpret_cast<u32x4 *>(base + q * 16) = v;
-            }
+        const int64_t nb = (t1 - t0) * a.E;
+        if ((nb & 15) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            for (int64_t q = tid; q < (nb >> 4); q += nthreads)
+                reinterpret_cast<u32x4 *>(base)[q] = z;
         } else {
-            const int64_t nb = (t1 - t0) * a.E;
-            for (int64_t q = tid; q < nb; q += nthreads) {
-                const int64_t t = t0 + q / a.E;
-                const int64_t e = q % a.E;
-                uint8_t v = 0;
-                for (int j = 0; j < k; ++j)
-                    v |= (id_at(idx, t * k + j) == e) ? 1 : 0;
-                base[q] = v;
-            }
+            for (int64_t q = tid; q < nb; q += nthreads)
+                base[q] = 0;
         }
     }
     if (a.probs) {
-        // routed weight at each routed expert; a repeated id adds its weight
-        // to the first one, in slot order
         float *base = a.probs + t0 * a.E;
-        const int width =
-            ((a.E & 3) == 0 && (reinterpret_cast<uintptr_t>(a.probs) & 15) == 0) ? 4 : 1;
-        const int cpt = a.E / width;
-        const int64_t nch = (t1 - t0) * cpt;
-        for (int64_t q = tid; q < nch; q += nthreads) {
-            const int64_t t = t0 + q / cpt;
-            const int eb = static_cast<int>(q % cpt) * width;
-            float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-            unsigned seen = 0;
-            for (int j = 0; j < k; ++j) {
-                const int64_t d = id_at(idx, t * k + j) - eb;
-                if (d >= 0 && d < width) {
-                    const float wj = a.w[t * k + j];
-                    const bool again = (seen >> d) & 1u;
-                    if (d == 0) v0 = again ? v0 + wj : wj;
-                    if (d == 1) v1 = again ? v1 + wj : wj;
-                    if (d == 2) v2 = again ? v2 + wj : wj;
-                    if (d == 3) v3 = again ? v3 + wj : wj;
-                    seen |= 1u << d;
-                }
-            }
-            if (width == 4) {
-                f32x4 v = {v0, v1, v2, v3};
-                *reinterpret_cast<f32x4 *>(base + q * 4) = v;
-            } else {
-                base[q] = v0;
-            }
+        const int64_t nf = (t1 - t0) * a.E;
+        if ((nf & 3) == 0 && (reinterpret_cast<uintptr_t>(base) & 15) == 0) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            for (int64_t q = tid; q < (nf >> 2); q += nthreads)
+                reinterpret_cast<f32x4 *>(base)[q] = z;
+        } else {
+            for (int64_t q = tid; q < nf; q += nthreads)
+                base[q] = 0.f;
         }
     }
     __syncthreads();
 
-    // Phase B: one thread per slot of the block's tokens.
-    const int64_t nslots = (t1 - t0) * k;
-    const int64_t s = t0 * k + tid;
-    int ep = -1;          // local expert of a primary local slot
-    int prim_back = 0;    // repeated id: distance back to its first slot
-    bool bad = false, dup = false, dup_local = false;
-    if (tid < nslots) {
-        const int64_t t = s / k;
-        const int j = static_cast<int>(s - t * k);
-        const int64_t e = id_at(idx, s);
-        bad = (e < -1) || (e >= a.E);
-        if (e >= 0 && e < a.E) {
-            for (int q = 0; q < j; ++q) {
-                if (id_at(idx, t * k + q) == e) {
-                    dup = true;
-                    prim_back = j - q;
-                    break;
-                }
-            }
-            if (e >= a.lb && e < static_cast<int64_t>(a.lb) + EL) {
-                if (dup)
-                    dup_local = true;
-                else
-                    ep = static_cast<int>(e - a.lb);
+    // One thread per slot: a repeated id points back at its first slot; the
+    // first slot of a local expert sets its bit in that expert's bitmap.
+    const bool bad = myid == -2;
+    bool dup = false;
+    int prim_back = 0, tl = 0, j = 0;
+    if (myid >= 0) {
+        tl = tid / k;
+        j = tid - tl * k;
+        for (int q = 0; q < j; ++q) {
+            if (sid[tl * k + q] == myid) {
+                dup = true;
+                prim_back = j - q;
+                break;
             }
         }
+    }
+    const int ep = (myid >= a.lb && myid < a.lb + EL) ? myid - a.lb : -1;
+    if (myid >= 0 && !dup) {
+        if (ep >= 0)
+            atomicOr(&bm[ep * W + (tid >> 5)], 1u << (tid & 31));
+        if (a.map)
+            a.map[(t0 + tl) * a.E + myid] = 1;
     }
     const uint64_t mbad = __ballot(bad);
     const uint64_t mdup = __ballot(dup);
     if (lane == 0 && (mbad | mdup))
         atomicOr(bflag, (mbad ? 1 : 0) | (mdup ? 2 : 0));
-
-    // Rank of each slot among the wave's slots of the same expert.  Lanes are
-    // in token order and a token holds at most one primary slot per expert,
-    // so the ballot prefix count is the ascending-token rank.
-    int my_rank = 0;
-    uint64_t rem = __ballot(ep >= 0);
-    while (rem) {
-        const int lead = __builtin_ctzll(rem);
-        const int e0 = __builtin_amdgcn_readlane(ep, lead);
-        const uint64_t m = __ballot(ep == e0);
-        if (ep == e0)
-            my_rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == 0)
-            cnt[wave * EL + e0] = __popcll(m);
-        rem &= ~m;
-    }
     __syncthreads();
 
-    // Exclusive prefix over waves per expert; block totals to the workspace.
+    const int bf = *bflag;
+    if (a.probs && myid >= 0 && !dup) {
+        // the first slot's weight plus later repeats of the id, in slot order
+        float wt = sw[tid];
+        if (bf & 2)
+            for (int q = j + 1; q < k; ++q)
+                if (sid[tl * k + q] == myid)
+                    wt = wt + sw[tl * k + q];
+        a.probs[(t0 + tl) * a.E + myid] = wt;
+    }
+    // Exclusive popcount prefix of each expert's bitmap; the total is the
+    // block's count for that expert.
     for (int e = tid; e < EL; e += nthreads) {
         int run = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            const int c = cnt[w * EL + e];
-            cnt[w * EL + e] = run;
-            run += c;
+        for (int w = 0; w < W; ++w) {
+            pref[e * W + w] = static_cast<uint16_t>(run);
+            run += __popc(bm[e * W + w]);
         }
         a.counts[b * EL + e] = run;
     }
     if (tid == 0)
-        a.blockflags[b] = *bflag;
+        a.blockflags[b] = bf;
     __syncthreads();
-    if (ep >= 0)
-        lrank[tid] = cnt[wave * EL + ep] + my_rank;
-    __syncthreads();
+
+    // In-block rank = earlier slots of the same expert = prefix + popcount of
+    // the bits below the owning slot (the first slot, for a repeated id).
     if (tid < nslots) {
         int v = -1;
-        if (ep >= 0)
-            v = lrank[tid];
-        else if (dup_local)
-            v = lrank[tid - prim_back]; // a repeated id shares its first slot's row
+        if (ep >= 0) {
+            const int p = tid - prim_back;
+            const int w = p >> 5;
+            const int r = pref[ep * W + w] + __popc(bm[ep * W + w] & ((1u << (p & 31)) - 1u));
+            v = (ep << kRankBits) | r;
+        }
         a.row_of_slot[s] = v;
     }
 }
 
 // ---------------------------------------------------------------------------
-// K2
+// block-wide scan helper (1024 threads)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 {
@@ -252,10 +231,133 @@ __device__ int block_incl_scan(int v, int *tmp)
     return v;
 }
 
+// Publish tokens_per_expert, offsets and the status word from LDS totals.
+// Called by every thread of one 1024-thread workgroup.  With a host alias of
+// the status (eager mode, pinned host memory), the status is also written
+// there with system-scope stores, so the host needs no copy after the sync.
+__device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, int *tmp, int flags)
+{
+    __shared__ int32_t st[4];
+    const int tid = threadIdx.x;
+    const int EL = a.EL;
+    const int cnt = tid < EL ? tot[tid] : 0;
+    const int padded = tid < EL ? ((cnt + a.P - 1) / a.P) * a.P : 0;
+    const int incl = block_incl_scan(padded, tmp);
+    const int data_incl = block_incl_scan(cnt, tmp);
+    if (tid < EL)
+        offl[tid] = incl - padded;
+    if (tid == EL - 1)
+        offl[EL] = incl;
+    if (a.status) {
+        if (tid < EL) {
+            a.tpe[tid] = cnt;
+            a.off[tid] = incl - padded;
+        }
+        if (tid == EL - 1) {
+            a.off[EL] = incl;
+            a.status[0] = incl;
+            a.status[2] = data_incl;
+            a.status[3] = 0;
+            st[0] = incl;
+            st[2] = data_incl;
+            st[3] = 0;
+        }
+        if (tid == 0) {
+            a.status[1] = flags;
+            st[1] = flags;
+        }
+    }
+    __syncthreads();
+    if (a.status && a.host_status && tid == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __hip_atomic_store(a.host_status + i, st[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __threadfence_system();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K2 (fused finish)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
+{
+    __shared__ int32_t pall[1024];  // [G][EL] partial totals
+    __shared__ int32_t pbef[1024];  // [G][EL] partial sums over blocks before this one
+    __shared__ int32_t offl[1025];  // offsets
+    __shared__ int32_t tmp[16];
+    __shared__ int32_t flag_s;
+    const int tid = threadIdx.x;
+    const int EL = a.EL;
+    const int64_t nblk = a.nblk;
+    const int64_t b = blockIdx.x;
+
+    if (tid == 0)
+        flag_s = 0;
+    __syncthreads();
+    if (b == 0) {
+        int f = 0;
+        for (int64_t bb = tid; bb < nblk; bb += 1024)
+            f |= a.blockflags[bb];
+        if (f)
+            atomicOr(&flag_s, f);
+    }
+    const int G = 1024 / EL;
+    const int g = tid / EL;
+    const int e = tid - g * EL;
+    if (g < G) {
+        const int64_t per = (nblk + G - 1) / G;
+        const int64_t b0 = static_cast<int64_t>(g) * per;
+        const int64_t b1 = min(nblk, b0 + per);
+        int all = 0, before = 0;
+#pragma unroll 8
+        for (int64_t bb = b0; bb < b1; ++bb) {
+            const int c = a.counts[bb * EL + e];
+            all += c;
+            before += bb < b ? c : 0;
+        }
+        pall[g * EL + e] = all;
+        pbef[g * EL + e] = before;
+    }
+    __syncthreads();
+    int tot_e = 0, base_e = 0;
+    if (tid < EL) {
+        for (int gg = 0; gg < G; ++gg) {
+            tot_e += pall[gg * EL + tid];
+            base_e += pbef[gg * EL + tid];
+        }
+    }
+    __syncthreads();
+    if (tid < EL) {
+        pall[tid] = tot_e;  // reuse: per-expert totals
+        pbef[tid] = base_e; // reuse: this block's per-expert base
+    }
+    __syncthreads();
+    RouteArgs pa = a;
+    if (b != 0)
+        pa.status = nullptr; // only block 0 publishes
+    publish(pa, pall, offl, tmp, flag_s);
+
+    const int64_t t0 = b * a.tokens_per_block;
+    const int64_t t1 = min(a.T, t0 + a.tokens_per_block);
+    const int nslots = static_cast<int>((t1 - t0) * a.k);
+    if (tid < nslots) {
+        const int64_t s = t0 * a.k + tid;
+        const int v = a.row_of_slot[s];
+        if (v >= 0) {
+            const int ex = packed_expert(v);
+            a.row_of_slot[s] = offl[ex] + pbef[ex] + packed_rank(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// large-T form: K2s scan (one workgroup), K3 rows (one thread per slot)
+// ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
 {
     __shared__ int32_t part[1024]; // [G][EL] group sums, then group bases
-    __shared__ int32_t tot[1024];  // per-expert totals
+    __shared__ int32_t tot[1024];
+    __shared__ int32_t offl[1025];
     __shared__ int32_t tmp[16];
     __shared__ int32_t flag_s;
     const int tid = threadIdx.x;
@@ -271,8 +373,7 @@ __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
     if (f)
         atomicOr(&flag_s, f);
 
-    // Blocks are split into G contiguous ranges; thread (g, e) sums range g.
-    const int G = EL >= 1024 ? 1 : 1024 / EL;
+    const int G = 1024 / EL;
     const int g = tid / EL;
     const int e = tid - g * EL;
     const int64_t per = (nblk + G - 1) / G;
@@ -294,9 +395,9 @@ __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
             run += c;
         }
         tot[tid] = run;
-        a.tpe[tid] = run;
     }
     __syncthreads();
+    publish(a, tot, offl, tmp, flag_s);
     if (g < G) {
         int run = part[g * EL + e];
         for (int64_t b = b0; b < b1; ++b) {
@@ -305,46 +406,26 @@ __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
             run += c;
         }
     }
-    const int cnt = tid < EL ? tot[tid] : 0;
-    const int padded = tid < EL ? ((cnt + a.P - 1) / a.P) * a.P : 0;
-    const int incl = block_incl_scan(padded, tmp);
-    const int data_incl = block_incl_scan(cnt, tmp);
-    if (tid < EL)
-        a.off[tid] = incl - padded;
-    if (tid == EL - 1) {
-        a.off[EL] = incl;
-        a.status[0] = incl;
-        a.status[2] = data_incl;
-        a.status[3] = 0;
-    }
-    if (tid == 0)
-        a.status[1] = flag_s;
 }
 
-// ---------------------------------------------------------------------------
-// K3
-// ---------------------------------------------------------------------------
-template <typename IT>
 __global__ void __launch_bounds__(256) k_route_rows(RouteArgs a)
 {
     const int64_t s = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (s >= a.T * a.k)
         return;
-    const int lr = a.row_of_slot[s];
-    if (lr < 0)
+    const int v = a.row_of_slot[s];
+    if (v < 0)
         return;
-    const IT *__restrict__ idx = static_cast<const IT *>(a.idx);
-    const int64_t t = s / a.k;
-    const int64_t b = t / a.tokens_per_block;
-    const int e = static_cast<int>(id_at(idx, s) - a.lb);
-    a.row_of_slot[s] = a.off[e] + a.counts[b * a.EL + e] + lr;
+    const int64_t b = (s / a.k) / a.tokens_per_block;
+    const int ex = packed_expert(v);
+    a.row_of_slot[s] = a.off[ex] + a.counts[b * a.EL + ex] + packed_rank(v);
 }
 
 hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
 {
     hipError_t err;
     if (a.nblk > 0) {
-        const size_t lds = (static_cast<size_t>(threads / kWave) * a.EL + threads + 1) * sizeof(int32_t);
+        const size_t lds = count_lds_bytes(threads, a.EL);
         if (a.idx_i64)
             k_route_count<int64_t><<<dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s>>>(a);
         else
@@ -352,16 +433,16 @@ hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }
+    if (a.nblk > 0 && a.nblk * a.EL <= kFusedFinishMax) {
+        k_route_finish<<<dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s>>>(a);
+        return hipGetLastError();
+    }
     k_route_scan<<<dim3(1), dim3(1024), 0, s>>>(a);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
     const int64_t nslots = a.T * a.k;
     if (nslots > 0) {
-        const unsigned grid = static_cast<unsigned>((nslots + 255) / 256);
-        if (a.idx_i64)
-            k_route_rows<int64_t><<<dim3(grid), dim3(256), 0, s>>>(a);
-        else
-            k_route_rows<int32_t><<<dim3(grid), dim3(256), 0, s>>>(a);
+        k_route_rows<<<dim3(static_cast<unsigned>((nslots + 255) / 256)), dim3(256), 0, s>>>(a);
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }

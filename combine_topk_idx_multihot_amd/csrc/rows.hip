@@ -2,31 +2,60 @@
 //
 // "Add the deepep expert-parallel implementation", "What this adds":
 //   "Expanded layout"  one row per (token, local expert) slot grouped by local
-//                      expert, each with its routing weight; the combine only
-//                      sums rows back to token order;
-//   "Eager vs captured" sync-free rows are sized for the worst case and rows
-//                      past the received total are zero and belong to a
-//                      sentinel expert;
+//                      expert, each with its routing weight; combine is a plain
+//                      sum of rows back to token order;
+//   "Eager vs captured" sync-free rows are sized for the worst case; rows past
+//                      the received total are zero and belong to a sentinel
+//                      expert;
 //   "Custom ops"       the combine's backward is a cached dispatch;
 //   "Training"         gradients reach the routing weights.
 //
 // All of it is HBM-bound data movement (no contraction, so no MFMA).  Design:
-//   * token-major: one wave per token; the wave reads the token's row once
-//     into VGPRs with 16-byte loads (64 lanes x 16 B = 1 KiB per instruction)
-//     and writes it to each of its local rows, so x is read from HBM once no
-//     matter how many local experts the token picked;
-//   * the token's k slots are handled lane-parallel (lane j = slot j): row
-//     lookup, repeated-id detection and weight merging are a few ballots and
-//     lane reads, no LDS;
+//   * token-major: the token's row is read from HBM once and written to each
+//     of its local rows (dispatch), or its local rows are gathered and added
+//     (combine).  The token's k slots sit one per lane: row lookup,
+//     repeated-id detection and weight merging are a few lane reads and
+//     ballots, no LDS.
+//   * a row is walked in segments of SEG 16-byte chunks per lane (SEG KiB
+//     per wave), and a token's segments are dealt over 1, 2 or 4 waves of the
+//     workgroup, so that even a few thousand tokens keep enough waves (and
+//     bytes) in flight on 256 CUs.  Within a segment a wave issues the loads
+//     of up to kBatch rows before consuming any of them.
+//   * the combine backward is the dispatch of grad_out plus the expert-output
+//     rows of the token's slots, reduced to fp64 dots: per lane over its
+//     segments, across the wave by butterfly, across the token's waves in LDS
+//     in a fixed order, so dw is the same on every run.
 //   * pad rows (one workgroup per expert) and the sentinel tail [total, R)
-//     (a grid-stride flat fill, since those rows are contiguous) are zeroed by
-//     extra workgroups of the same launch, so the fill overlaps the gather;
-//   * combine is token-major too: the wave gathers its token's rows (the next
-//     row's loads are issued before the current one is added) and adds them in
-//     fp32 in ascending slot order, then writes bf16 (nearest-even) or fp32.
+//     are zeroed by extra workgroups of the same launch.  The tail is one
+//     contiguous range, cut into 64 KiB wave tasks: a contiguous stream per
+//     wave writes HBM markedly faster than a grid-stride pattern on MI355X.
+//   * combine adds the token's rows in fp32 in ascending slot order (the
+//     accumulator starts from the first row) and writes bf16 (nearest-even)
+//     or fp32; one wave per (token, segment), gather loads non-temporal
+//     (those rows are read once).
 #include "moe_internal.h"
 
+#ifndef MOE_COMBINE_SEG
+#define MOE_COMBINE_SEG 2
+#endif
+#ifndef MOE_BWD_SEG
+#define MOE_BWD_SEG 2
+#endif
+#ifndef MOE_COPY_SEG
+#define MOE_COPY_SEG 2
+#endif
+#ifndef MOE_MAX_WPT
+#define MOE_MAX_WPT 4
+#endif
+#ifndef MOE_NT_ZERO
+#define MOE_NT_ZERO 1
+#endif
+
+
 namespace moe {
+
+constexpr int kBatch = 8;            // rows whose loads are in flight together
+constexpr int64_t kZeroTask = 4096;  // 16-byte chunks (64 KiB) per zero-fill wave task
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -43,55 +72,136 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+template <bool NT>
+__device__ __forceinline__ void put16(u32x4 *p, const u32x4 &v)
+{
+    if (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 // The token's slots, one per lane: its row (or -1), whether the row is valid
-// (inside [0, R)), whether the lane is the first slot naming that row, and the
-// lane of that first slot.
+// (inside [0, R)), and the lane of the first slot naming that row.
 struct Slots {
     int row;
     bool valid;
-    bool prim;
     int first;
-    uint64_t prim_mask;
-    uint64_t dup_mask;
+    uint64_t prim_mask; // lanes that are the first slot of their row
+    uint64_t dup_mask;  // valid lanes that repeat an earlier slot's row
 };
 
 __device__ __forceinline__ Slots load_slots(const int32_t *__restrict__ row_of_slot, int64_t t,
-                                            int k, int64_t R, int lane)
+                                            int k, int64_t R, int lane, bool active)
 {
     Slots s;
-    s.row = lane < k ? row_of_slot[t * k + lane] : -1;
-    s.valid = lane < k && s.row >= 0 && s.row < R;
+    s.row = (active && lane < k) ? row_of_slot[t * k + lane] : -1;
+    s.valid = active && lane < k && s.row >= 0 && s.row < R;
     s.first = lane;
     for (int q = 0; q < k; ++q) {
         const int rq = __builtin_amdgcn_readlane(s.row, q);
         if (q < lane && s.valid && rq == s.row && s.first == lane)
             s.first = q;
     }
-    s.prim = s.valid && s.first == lane;
-    s.prim_mask = __ballot(s.prim);
-    s.dup_mask = __ballot(s.valid && !s.prim);
+    const bool prim = s.valid && s.first == lane;
+    s.prim_mask = __ballot(prim);
+    s.dup_mask = __ballot(s.valid && !prim);
     return s;
+}
+
+// Up to kBatch slots taken (ascending) off a lane mask: their lanes and rows
+// (wave-uniform values).
+struct Batch {
+    int n;
+    int lane[kBatch];
+    int64_t row[kBatch];
+};
+
+__device__ __forceinline__ Batch take_batch(uint64_t &m, int row)
+{
+    Batch bt;
+    bt.n = 0;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+        bt.lane[b] = 0;
+        bt.row[b] = 0;
+        if (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            bt.lane[b] = j;
+            bt.row[b] = __builtin_amdgcn_readlane(row, j);
+            bt.n = b + 1;
+        }
+    }
+    return bt;
+}
+
+// NT: non-temporal loads, for rows read once (the combine's gather).
+template <int SEG, bool NT = false>
+__device__ __forceinline__ void load_seg(u32x4 (&v)[SEG], const uint16_t *base, int64_t r, int H,
+                                         int c0, int nch, int lane)
+{
+    const u32x4 *__restrict__ p = reinterpret_cast<const u32x4 *>(base + r * H);
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (c < nch) {
+            if (NT)
+                v[i] = __builtin_nontemporal_load(p + c);
+            else
+                v[i] = p[c];
+        }
+    }
+}
+
+// Zero the 16-byte chunks [q0, q1) of `dst` in wave tasks of kZeroTask
+// contiguous chunks; wave `w` of `nw` takes tasks w, w + nw, ...
+__device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0, int64_t q1, int64_t w,
+                                            int64_t nw, int lane)
+{
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int64_t ntask = (q1 - q0 + kZeroTask - 1) / kZeroTask;
+    for (int64_t task = w; task < ntask; task += nw) {
+        const int64_t b = q0 + task * kZeroTask;
+        const int64_t e = min(q1, b + kZeroTask);
+        int64_t i = b + lane;
+        for (; i + 3 * kWave < e; i += 4 * kWave) {
+            put16<MOE_NT_ZERO != 0>(dst + i, z);
+            put16<MOE_NT_ZERO != 0>(dst + i + kWave, z);
+            put16<MOE_NT_ZERO != 0>(dst + i + 2 * kWave, z);
+            put16<MOE_NT_ZERO != 0>(dst + i + 3 * kWave, z);
+        }
+        for (; i < e; i += kWave)
+            put16<MOE_NT_ZERO != 0>(dst + i, z);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // dispatch / combine backward
 // ---------------------------------------------------------------------------
-template <int NCH, bool DOT>
+template <int SEG, bool DOT>
 __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
 {
-    __shared__ double dotacc[kRowWaves][kMaxK];
+    __shared__ double red[kRowWaves][kBatch]; // per-wave dot partials (DOT)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = bid * kRowWaves + wave;
-    if (t >= a.T)
+    const int nwt = a.waves_per_token;
+    const int tl = wave / nwt;        // token of this wave inside the workgroup
+    const int wt = wave - tl * nwt;   // this wave's share of the token's segments
+    const int64_t t = bid * (kRowWaves / nwt) + tl;
+    const bool active = t < a.T;
+    // DOT uses workgroup barriers, so every wave runs the same number of
+    // batch rounds, active or not; without DOT idle waves just leave.
+    if (!DOT && !active)
         return;
     const int k = a.k;
-    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane);
+    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, active);
+    const bool prim = sl.valid && sl.first == lane;
 
-    // metadata of the token's rows (dispatch only)
-    if (a.row_w || a.row_token) {
+    // metadata of the token's rows (dispatch only), by the token's first wave
+    if (wt == 0 && (a.row_w || a.row_token)) {
         float W = 0.f;
-        if (a.topk_w) {
+        if (a.topk_w && active) {
             const float myw = lane < k ? a.topk_w[t * k + lane] : 0.f;
             W = myw;
             if (sl.dup_mask) {
@@ -99,12 +209,12 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
                 for (int q = 0; q < k; ++q) {
                     const int rq = __builtin_amdgcn_readlane(sl.row, q);
                     const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), q));
-                    if (sl.prim && q > lane && rq == sl.row)
+                    if (prim && q > lane && rq == sl.row)
                         W = W + wq;
                 }
             }
         }
-        if (sl.prim) {
+        if (prim) {
             if (a.row_token)
                 a.row_token[sl.row] = static_cast<int32_t>(t);
             if (a.row_w)
@@ -112,78 +222,95 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
         }
     }
 
-    if (DOT) {
-        if (lane < k)
-            dotacc[wave][lane] = 0.0;
-    }
-    if (sl.prim_mask) {
-        const int nch = a.H >> 3; // 16-byte chunks per row
-        const u32x4 *__restrict__ src = reinterpret_cast<const u32x4 *>(a.src + t * a.H);
-        for (int c0 = 0; c0 < nch; c0 += NCH * kWave) {
-            u32x4 v[NCH];
+    float mydw = 0.f;
+    const int nch = a.H >> 3; // 16-byte chunks per row
+    constexpr int SPAN = SEG * kWave;
+    const int nseg = (nch + SPAN - 1) / SPAN;
+    const int rounds = DOT ? (k + kBatch - 1) / kBatch : 0;
+    uint64_t mrest = sl.prim_mask;
+    for (int ib = 0; DOT ? ib < rounds : mrest != 0; ++ib) {
+        const Batch bt = take_batch(mrest, sl.row);
+        double part[kBatch];
 #pragma unroll
-            for (int i = 0; i < NCH; ++i) {
-                const int c = c0 + i * kWave + lane;
-                if (c < nch)
-                    v[i] = src[c];
-            }
-            uint64_t m = sl.prim_mask;
-            while (m) {
-                const int j = __builtin_ctzll(m);
-                m &= m - 1;
-                const int64_t r = __builtin_amdgcn_readlane(sl.row, j);
-                u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + r * a.H);
+        for (int b = 0; b < kBatch; ++b)
+            part[b] = 0.0;
+        if (bt.n > 0) {
+            for (int sg = wt; sg < nseg; sg += nwt) {
+                const int c0 = sg * SPAN;
+                u32x4 v[SEG];
+                load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
+                u32x4 f[DOT ? kBatch : 1][SEG];
                 if (DOT) {
-                    const u32x4 *__restrict__ fr = reinterpret_cast<const u32x4 *>(a.F + r * a.H);
-                    u32x4 fv[NCH];
 #pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        const int c = c0 + i * kWave + lane;
-                        if (c < nch)
-                            fv[i] = fr[c];
-                    }
+                    for (int b = 0; b < kBatch; ++b)
+                        if (b < bt.n)
+                            load_seg<SEG>(f[DOT ? b : 0], a.F, bt.row[b], a.H, c0, nch, lane);
+                }
 #pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        const int c = c0 + i * kWave + lane;
-                        if (c < nch)
-                            dst[c] = v[i];
-                    }
-                    double acc = 0.0;
+                for (int b = 0; b < kBatch; ++b) {
+                    if (b < bt.n) {
+                        u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + bt.row[b] * a.H);
 #pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        const int c = c0 + i * kWave + lane;
-                        if (c < nch) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                acc = fma(static_cast<double>(bf16_lo(v[i][q])),
-                                          static_cast<double>(bf16_lo(fv[i][q])), acc);
-                                acc = fma(static_cast<double>(bf16_hi(v[i][q])),
-                                          static_cast<double>(bf16_hi(fv[i][q])), acc);
-                            }
+                        for (int i = 0; i < SEG; ++i) {
+                            const int c = c0 + i * kWave + lane;
+                            if (c < nch)
+                                dst[c] = v[i];
                         }
                     }
+                }
+                if (DOT) {
 #pragma unroll
-                    for (int o = kWave / 2; o >= 1; o >>= 1)
-                        acc += __shfl_xor(acc, o);
-                    if (lane == 0)
-                        dotacc[wave][j] += acc;
-                } else {
+                    for (int b = 0; b < kBatch; ++b) {
+                        if (b < bt.n) {
 #pragma unroll
-                    for (int i = 0; i < NCH; ++i) {
-                        const int c = c0 + i * kWave + lane;
-                        if (c < nch)
-                            dst[c] = v[i];
+                            for (int i = 0; i < SEG; ++i) {
+                                const int c = c0 + i * kWave + lane;
+                                if (c < nch) {
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) {
+                                        const uint32_t gw = v[i][q], fw = f[DOT ? b : 0][i][q];
+                                        part[b] = fma(static_cast<double>(bf16_lo(gw)),
+                                                      static_cast<double>(bf16_lo(fw)), part[b]);
+                                        part[b] = fma(static_cast<double>(bf16_hi(gw)),
+                                                      static_cast<double>(bf16_hi(fw)), part[b]);
+                                    }
+                                }
+                            }
+                        }
                     }
                 }
             }
         }
+        if (DOT) {
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (b < bt.n) {
+                    double s = part[b];
+#pragma unroll
+                    for (int o = kWave / 2; o >= 1; o >>= 1)
+                        s += __shfl_xor(s, o);
+                    if (lane == 0)
+                        red[wave][b] = s;
+                }
+            }
+            __syncthreads();
+            if (wt == 0) {
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b) {
+                    if (b < bt.n) {
+                        double s = red[wave][b];
+                        for (int w = 1; w < nwt; ++w)
+                            s += red[wave + w][b];
+                        if (sl.valid && sl.first == bt.lane[b])
+                            mydw = static_cast<float>(s);
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
-    if (DOT && a.dw) {
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        if (lane < k)
-            a.dw[t * k + lane] = sl.valid ? static_cast<float>(dotacc[wave][sl.first]) : 0.f;
-    }
+    if (DOT && a.dw && active && wt == 0 && lane < k)
+        a.dw[t * k + lane] = sl.valid ? mydw : 0.f;
 }
 
 // Pad rows of one expert's group: zero data, token -1, weight 0; every row of
@@ -205,10 +332,8 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
             a.row_w[r] = 0.f;
     }
     const int64_t nch = a.H >> 3;
-    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t q = pad0 * nch + tid; q < hi * nch; q += kRowThreads)
-        dst[q] = z;
+    zero_chunks(reinterpret_cast<u32x4 *>(a.rows), pad0 * nch, hi * nch, threadIdx.x / kWave,
+                kRowWaves, tid & (kWave - 1));
 }
 
 // Rows [total, R): zero data, token -1, expert EL (the sentinel), weight 0.
@@ -230,119 +355,106 @@ __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
             a.row_w[r] = 0.f;
     }
     const int64_t nch = a.H >> 3;
-    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int64_t q1 = r1 * nch;
-    for (int64_t q = r0 * nch + gtid; q < q1; q += gstride)
-        dst[q] = z;
+    const int64_t wave = sb * kRowWaves + (threadIdx.x / kWave);
+    zero_chunks(reinterpret_cast<u32x4 *>(a.rows), r0 * nch, r1 * nch, wave,
+                a.nsent_blocks * kRowWaves, threadIdx.x & (kWave - 1));
 }
 
-template <int NCH, bool DOT>
+// Grid: [sentinel blocks][token blocks][expert blocks].  The sentinel tail
+// (all of the worst-case rows past total) is the longest-running part in
+// sync-free mode, so its workgroups are dispatched first.
+template <int SEG, bool DOT>
 __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 {
-    const int64_t bid = blockIdx.x;
-    if (bid < a.ntok_blocks)
-        move_token<NCH, DOT>(a, bid);
-    else if (bid < a.ntok_blocks + a.nexp_blocks)
-        fill_expert(a, static_cast<int>(bid - a.ntok_blocks));
-    else
-        fill_sentinel(a, bid - a.ntok_blocks - a.nexp_blocks);
-}
-
-// ---------------------------------------------------------------------------
-// combine
-// ---------------------------------------------------------------------------
-template <int NCH>
-__device__ __forceinline__ void load_row(u32x4 (&v)[NCH], const uint16_t *base, int64_t r, int H,
-                                         int c0, int nch, int lane)
-{
-    const u32x4 *__restrict__ p = reinterpret_cast<const u32x4 *>(base + r * H);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-        const int c = c0 + i * kWave + lane;
-        if (c < nch)
-            v[i] = p[c];
+    int64_t bid = blockIdx.x;
+    if (bid < a.nsent_blocks) {
+        fill_sentinel(a, bid);
+        return;
     }
+    bid -= a.nsent_blocks;
+    if (bid < a.ntok_blocks)
+        move_token<SEG, DOT>(a, bid);
+    else
+        fill_expert(a, static_cast<int>(bid - a.ntok_blocks));
 }
 
-template <int NCH, bool OUT_F32>
+// ---------------------------------------------------------------------------
+// combine: one wave per (token, segment); the waves of a workgroup read all
+// segments of a token's rows at about the same time
+// ---------------------------------------------------------------------------
+template <int SEG, bool OUT_F32>
 __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kRowWaves + wave;
-    if (t == 0 && lane == 0 && a.eager && a.status[0] != a.R)
+    const int nch = a.H >> 3;
+    constexpr int SPAN = SEG * kWave;
+    const int nseg = (nch + SPAN - 1) / SPAN;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kRowWaves + wave;
+    const int64_t t = gw / nseg;
+    const int c0 = static_cast<int>(gw - t * nseg) * SPAN;
+    if (gw == 0 && lane == 0 && a.eager && a.status[0] != a.R)
         atomicOr(&a.status[1], 4);
     if (t >= a.T)
         return;
-    const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane);
-    const int nch = a.H >> 3;
-    for (int c0 = 0; c0 < nch; c0 += NCH * kWave) {
-        float acc[NCH][8];
-        uint64_t m = sl.prim_mask;
-        if (!m) {
+    const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
+    float acc[SEG][8];
 #pragma unroll
-            for (int i = 0; i < NCH; ++i)
+    for (int i = 0; i < SEG; ++i)
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    acc[i][q] = 0.f;
-        } else {
-            u32x4 cur[NCH];
-            int j = __builtin_ctzll(m);
-            m &= m - 1;
-            load_row<NCH>(cur, a.Y, __builtin_amdgcn_readlane(sl.row, j), a.H, c0, nch, lane);
-            bool first = true;
-            while (true) {
-                const bool more = m != 0;
-                u32x4 nxt[NCH];
-                if (more) {
-                    j = __builtin_ctzll(m);
-                    m &= m - 1;
-                    load_row<NCH>(nxt, a.Y, __builtin_amdgcn_readlane(sl.row, j), a.H, c0, nch, lane);
-                }
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.f;
+    bool first = true;
+    uint64_t mrest = sl.prim_mask;
+    while (mrest) {
+        const Batch bt = take_batch(mrest, sl.row);
+        u32x4 f[kBatch][SEG];
 #pragma unroll
-                for (int i = 0; i < NCH; ++i) {
+        for (int b = 0; b < kBatch; ++b)
+            if (b < bt.n)
+                load_seg<SEG, true>(f[b], a.Y, bt.row[b], a.H, c0, nch, lane);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            if (b < bt.n) {
+#pragma unroll
+                for (int i = 0; i < SEG; ++i) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float lo = bf16_lo(cur[i][q]);
-                        const float hi = bf16_hi(cur[i][q]);
+                        const float lo = bf16_lo(f[b][i][q]);
+                        const float hi = bf16_hi(f[b][i][q]);
                         acc[i][2 * q] = first ? lo : acc[i][2 * q] + lo;
                         acc[i][2 * q + 1] = first ? hi : acc[i][2 * q + 1] + hi;
                     }
                 }
                 first = false;
-                if (!more)
-                    break;
-#pragma unroll
-                for (int i = 0; i < NCH; ++i)
-                    cur[i] = nxt[i];
             }
         }
+    }
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int c = c0 + i * kWave + lane;
-            if (c >= nch)
-                continue;
-            if (OUT_F32) {
-                f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + t * a.H) + 2 * c;
-                const f32x4 v0 = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-                const f32x4 v1 = {acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
-                o[0] = v0;
-                o[1] = v1;
-            } else {
-                u32x4 v;
+    for (int i = 0; i < SEG; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (c >= nch)
+            continue;
+        if (OUT_F32) {
+            f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + t * a.H) + 2 * c;
+            const f32x4 v0 = {acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+            const f32x4 v1 = {acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+            o[0] = v0;
+            o[1] = v1;
+        } else {
+            u32x4 v;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    v[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
-                reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) + t * a.H)[c] = v;
-            }
+            for (int q = 0; q < 4; ++q)
+                v[q] = bf16_rne(acc[i][2 * q]) | (bf16_rne(acc[i][2 * q + 1]) << 16);
+            reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) + t * a.H)[c] = v;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// launchers
+// launch shapes
 // ---------------------------------------------------------------------------
+// 16-byte chunks per lane that cover one row (power of two, at most 16).
 static int chunks_per_lane(int H)
 {
     const int nch = H >> 3;
@@ -353,15 +465,42 @@ static int chunks_per_lane(int H)
     return n;
 }
 
-template <bool DOT>
-static void launch_move(int nch, dim3 g, const RowArgs &a, hipStream_t s)
+// Sentinel-fill workgroups: sync-free mode sizes them for the whole
+// worst-case tail, about four 64 KiB zero tasks per wave; eager mode keeps a
+// handful for the (normally empty) [total, R).
+static int64_t sentinel_blocks(const RowArgs &a)
 {
-    switch (nch) {
+    if (a.R <= 0)
+        return a.eager ? 1 : 0;
+    if (a.eager)
+        return 8;
+    const int64_t bytes = a.R * static_cast<int64_t>(a.H) * 2;
+    const int64_t tasks = (bytes + 65535) / 65536;
+    const int64_t nb = (tasks + 4 * kRowWaves - 1) / (4 * kRowWaves);
+    return nb < 1 ? 1 : (nb > 4096 ? 4096 : nb);
+}
+
+void row_shape(RowArgs &a)
+{
+    const int whole = chunks_per_lane(a.H);
+    const int cap = a.dw ? MOE_BWD_SEG : MOE_COPY_SEG;
+    a.seg = whole < cap ? whole : cap;
+    const int nch = a.H >> 3;
+    const int nseg = (nch + a.seg * kWave - 1) / (a.seg * kWave);
+    a.waves_per_token = nseg >= 4 && MOE_MAX_WPT >= 4 ? 4 : (nseg >= 2 && MOE_MAX_WPT >= 2 ? 2 : 1);
+    const int64_t tpb = kRowWaves / a.waves_per_token;
+    a.ntok_blocks = (a.T + tpb - 1) / tpb;
+    a.nexp_blocks = a.R > 0 ? a.EL : 0;
+    a.nsent_blocks = sentinel_blocks(a);
+}
+
+template <bool DOT>
+static void launch_move(int seg, dim3 g, const RowArgs &a, hipStream_t s)
+{
+    switch (seg) {
     case 1: k_move_rows<1, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
     case 2: k_move_rows<2, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 4: k_move_rows<4, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 8: k_move_rows<8, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    default: k_move_rows<16, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    default: k_move_rows<4, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
     }
 }
 
@@ -371,37 +510,37 @@ hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
     if (nb == 0)
         return hipSuccess;
     const dim3 g(static_cast<unsigned>(nb));
-    const int nch = chunks_per_lane(a.H);
     if (a.dw)
-        launch_move<true>(nch, g, a, s);
+        launch_move<true>(a.seg, g, a, s);
     else
-        launch_move<false>(nch, g, a, s);
+        launch_move<false>(a.seg, g, a, s);
     return hipGetLastError();
 }
 
 template <bool F32>
-static void launch_comb(int nch, dim3 g, const CombineArgs &a, hipStream_t s)
+static void launch_comb(int seg, dim3 g, const CombineArgs &a, hipStream_t s)
 {
-    switch (nch) {
+    switch (seg) {
     case 1: k_combine<1, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
     case 2: k_combine<2, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 4: k_combine<4, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 8: k_combine<8, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    default: k_combine<16, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    default: k_combine<4, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
     }
 }
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
 {
-    const int64_t nb = (a.T + kRowWaves - 1) / kRowWaves;
+    const int whole = chunks_per_lane(a.H);
+    const int seg = whole < MOE_COMBINE_SEG ? whole : MOE_COMBINE_SEG;
+    const int64_t span = static_cast<int64_t>(seg) * kWave;
+    const int64_t nseg = ((a.H >> 3) + span - 1) / span;
+    const int64_t nb = (a.T * nseg + kRowWaves - 1) / kRowWaves;
     if (nb == 0)
         return hipSuccess;
     const dim3 g(static_cast<unsigned>(nb));
-    const int nch = chunks_per_lane(a.H);
     if (a.out_f32)
-        launch_comb<true>(nch, g, a, s);
+        launch_comb<true>(seg, g, a, s);
     else
-        launch_comb<false>(nch, g, a, s);
+        launch_comb<false>(seg, g, a, s);
     return hipGetLastError();
 }
 

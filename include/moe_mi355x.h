@@ -86,8 +86,10 @@ typedef struct moe_desc {
     int64_t capacity;     /* MOE_SYNC_FREE: rows C >= T*min(k,EL) + EL*(P-1); else ignored */
 } moe_desc;
 
-/* The dispatch handle: plain device tensors, so it can travel through an op
- * boundary as tensors and be rebuilt ("Custom ops").  Caller-owned. */
+/* The dispatch handle: plain device buffers, so it can travel through an op
+ * boundary as tensors and be rebuilt ("Custom ops").  Caller-owned; written by
+ * moe_route_build and read by the calls after it, so it must stay alive and
+ * unchanged until the last of them has run on the stream. */
 typedef struct moe_handle {
     uint8_t *routing_map;       /* [T,E] u8 multihot map, or NULL to skip writing it */
     int32_t *tokens_per_expert; /* [EL] exact (unpadded) routes per local expert */
@@ -95,13 +97,17 @@ typedef struct moe_handle {
     int32_t *row_of_slot;       /* [T,k] row of each slot, -1 if invalid or not local;
                                    repeated ids point at the first slot's row */
     int32_t *status;            /* [4] {total, flags (MOE_FLAG_*), data rows, 0} */
+    void *workspace;            /* >= moe_route_workspace_size(desc) bytes of device
+                                   scratch for moe_route_build (per-block counts) */
+    size_t workspace_bytes;
 } moe_handle;
 
 /* Smallest legal sync-free capacity: T*min(k,EL) + EL*(P-1) (worst case: every
  * token routes all of its slots locally and every group needs P-1 pad rows). */
 int64_t moe_capacity_min(const moe_desc *desc);
 
-/* Device bytes moe_route_build needs as scratch (per-block counts). */
+/* Device bytes of handle.workspace for this description (0 if the description
+ * is invalid): about ceil(T*k/1024) * (EL + 1) * 4 bytes. */
 size_t moe_route_workspace_size(const moe_desc *desc);
 
 /*
@@ -114,17 +120,18 @@ size_t moe_route_workspace_size(const moe_desc *desc);
  *   topk_w          device [T,k] fp32 or NULL; needed only for multihot_probs.
  *   multihot_probs  device [T,E] fp32 or NULL: the routed weight at each routed
  *                   expert (repeated ids summed in slot order), 0 elsewhere.
- *   handle          outputs (see moe_handle); status is fully rewritten.
- *   workspace       device scratch of >= moe_route_workspace_size bytes.
+ *   handle          outputs (see moe_handle); status is fully rewritten; its
+ *                   workspace must hold moe_route_workspace_size bytes.
  *   host_status     host int32[4]: MOE_EAGER receives {total, flags, data rows, 0}
- *                   after the one stream sync (pinned memory makes the copy a
- *                   plain DMA); MOE_SYNC_FREE: unused, may be NULL.
+ *                   after the one stream sync.  Pinned memory is written by the
+ *                   kernel directly; pageable memory gets a copy after it.
+ *                   MOE_SYNC_FREE: unused, may be NULL.
  * Rows inside an expert's group are in ascending token order.  Returns
  * MOE_ERR_INDEX in eager mode when MOE_FLAG_BAD_ID is set (outputs valid).
  */
 int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                    float *multihot_probs, const moe_handle *handle, void *workspace,
-                    size_t workspace_bytes, int32_t *host_status, void *stream);
+                    float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                    void *stream);
 
 /*
  * Dispatch into the expanded layout ("Expanded layout"; "Eager vs captured").

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 def test_desc_struct_layout_matches_header():
     assert ctypes.sizeof(B.Desc) == 48
     assert B.Desc.capacity.offset == 40
-    assert ctypes.sizeof(B._Handle) == 5 * 8
+    assert ctypes.sizeof(B._Handle) == 7 * 8
 
 
 def _desc(**kw):
@@ -45,16 +45,15 @@ def _desc(**kw):
     return B.make_desc(**base)
 
 
-def _handle():
+def _handle(ws_bytes=1 << 30):
     h = B._Handle(routing_map=FAKE, tokens_per_expert=FAKE, padded_offsets=FAKE,
-                  row_of_slot=FAKE, status=FAKE)
+                  row_of_slot=FAKE, status=FAKE, workspace=FAKE, workspace_bytes=ws_bytes)
     return h
 
 
-def route_rc(d, ws_bytes=1 << 20, idx=FAKE, w=None, probs=None, host=FAKE, handle=None):
-    h = handle if handle is not None else _handle()
-    return B.lib().moe_route_build(ctypes.byref(d), idx, w, probs, ctypes.byref(h), FAKE, ws_bytes,
-                                   host, None)
+def route_rc(d, ws_bytes=1 << 30, idx=FAKE, w=None, probs=None, host=FAKE, handle=None):
+    h = handle if handle is not None else _handle(ws_bytes)
+    return B.lib().moe_route_build(ctypes.byref(d), idx, w, probs, ctypes.byref(h), host, None)
 
 
 def dispatch_rc(d, H=2048, R=10, x=FAKE, rows=FAKE, w=None, row_w=None):
@@ -125,6 +124,12 @@ def test_workspace_rules():
     need = B.moe_route_workspace_size(d)
     assert need > 0
     assert route_rc(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+    h = _handle(need - 1)
+    assert B.lib().moe_dispatch(ctypes.byref(d), ctypes.byref(h), FAKE, 2048, None, 10, FAKE, None,
+                                None, None, None) == B.MOE_ERR_WORKSPACE
+    h = _handle()
+    h.workspace = None
+    assert route_rc(d, handle=h) == B.MOE_ERR_WORKSPACE
     assert B.lib().moe_route_workspace_size(ctypes.byref(_desc(k=0))) == 0
 
 

@@ -60,10 +60,9 @@ class Run:
         x_t = to_dev_bf16(x)
         self.rc = B.MOE_OK
         h = B.alloc_handle(d)
-        ws = B.workspace_for(d)
         probs = torch.empty((T, E), dtype=torch.float32, device="cuda") if want_probs else None
         try:
-            B.moe_route_build(d, idx_t, h, ws, w_t if want_probs else None, probs)
+            B.moe_route_build(d, idx_t, h, w_t if want_probs else None, probs)
         except B.MoeError as e:
             self.rc = e.code
         torch.cuda.synchronize()
@@ -290,7 +289,6 @@ def test_graph_capture_replays_like_eager():
     g_t = to_dev_bf16(inputs.bf16_normal((T, H), rng))
     F_t = to_dev_bf16(inputs.bf16_normal((C, H), rng))
     h = B.alloc_handle(d)
-    ws = B.workspace_for(d)
     rows = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
     row_w = torch.empty(C, dtype=torch.float32, device="cuda")
     out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
@@ -298,7 +296,7 @@ def test_graph_capture_replays_like_eager():
     dw = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
 
     def step(stream=None):
-        B.moe_route_build(d, idx_t, h, ws, stream=stream)
+        B.moe_route_build(d, idx_t, h, stream=stream)
         B.moe_dispatch(d, h, x_t, H, C, rows, w_t, row_w, stream=stream)
         B.moe_combine(d, h, rows, H, C, out, stream=stream)
         B.moe_combine_bwd(d, h, g_t, H, C, gr, F_t, dw, stream=stream)
