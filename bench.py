@@ -214,10 +214,40 @@ def main():
                      "frac": round(kern[dominant]["GBps"] / PEAK_GBS, 4), "traffic": None},
     }
 
+    result["roofline"]["traffic"] = measured_traffic(wl.name, dominant)
+
     # ---- CPU baseline: the oracle on the host, bounded sample ---------------
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, sets[0], args.cpu_seconds, torch)
     print(json.dumps(result), flush=True)
+
+
+def kernel_source_sha256():
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "combine_topk_idx_multihot_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/traffic.json, counters scaled by a plain copy
+    of known size); None if there is none for this workload or if the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_sha256():
+        return None
+    k = t.get("workloads", {}).get(workload, {}).get(kernel)
+    return None if k is None else int(k["bytes"])
 
 
 def calibrate_copy(mib):

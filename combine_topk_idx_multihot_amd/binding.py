@@ -113,15 +113,28 @@ def _dev(t: torch.Tensor | None, name: str, dtype, numel: int, optional: bool = 
         if optional:
             return None
         raise MoeError(MOE_ERR_ARG, f"{name} is required")
+    try:
+        ok = t.is_cuda and t.dtype in dtype and t.is_contiguous() and t.numel() >= numel
+    except (AttributeError, TypeError):
+        ok = False
+    if not ok:
+        _explain(t, name, dtype, numel)
+    return t.data_ptr()
+
+
+def _explain(t, name, dtype, numel):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise MoeError(MOE_ERR_ARG, f"{name} must be a GPU tensor")
-    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
-        raise MoeError(MOE_ERR_ARG, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dtype not in dtype:
+        raise MoeError(MOE_ERR_ARG, f"{name} has dtype {t.dtype}, expected one of {dtype}")
     if not t.is_contiguous():
         raise MoeError(MOE_ERR_ARG, f"{name} must be contiguous")
-    if t.numel() < numel:
-        raise MoeError(MOE_ERR_ARG, f"{name} has {t.numel()} elements, needs {numel}")
-    return t.data_ptr()
+    raise MoeError(MOE_ERR_ARG, f"{name} has {t.numel()} elements, needs {numel}")
+
+
+# dtype sets accepted by _dev
+_U8, _I32, _I64, _F32, _BF16 = ((torch.uint8,), (torch.int32,), (torch.int64,), (torch.float32,),
+                                (torch.bfloat16,))
 
 
 def _stream(stream) -> int:
@@ -145,17 +158,30 @@ class Handle:
     workspace: torch.Tensor            # [moe_route_workspace_size] uint8 (device)
 
     def c(self) -> _Handle:
+        """The C struct, checked and built once: a Handle's tensors are not to
+        be reassigned after creation (build a new Handle instead)."""
+        cs = self.__dict__.get("_cstruct")
+        if cs is not None:
+            return cs
         d = self.desc
-        return _Handle(
-            workspace=_dev(self.workspace, "workspace", torch.uint8, moe_route_workspace_size(d)),
+        cs = _Handle(
+            workspace=_dev(self.workspace, "workspace", _U8, moe_route_workspace_size(d)),
             workspace_bytes=self.workspace.numel(),
-            routing_map=_dev(self.routing_map, "routing_map", torch.uint8, d.T * d.E, True),
-            tokens_per_expert=_dev(self.tokens_per_expert, "tokens_per_expert", torch.int32,
-                                   d.num_local),
-            padded_offsets=_dev(self.padded_offsets, "padded_offsets", torch.int32,
-                                d.num_local + 1),
-            row_of_slot=_dev(self.row_of_slot, "row_of_slot", torch.int32, d.T * d.k),
-            status=_dev(self.status, "status", torch.int32, 4))
+            routing_map=_dev(self.routing_map, "routing_map", _U8, d.T * d.E, True),
+            tokens_per_expert=_dev(self.tokens_per_expert, "tokens_per_expert", _I32, d.num_local),
+            padded_offsets=_dev(self.padded_offsets, "padded_offsets", _I32, d.num_local + 1),
+            row_of_slot=_dev(self.row_of_slot, "row_of_slot", _I32, d.T * d.k),
+            status=_dev(self.status, "status", _I32, 4))
+        hs = self.host_status
+        if hs.is_cuda or hs.dtype != torch.int32 or hs.numel() < 4 or not hs.is_contiguous():
+            raise MoeError(MOE_ERR_ARG, "host_status must be a host int32 tensor of 4 elements")
+        self.__dict__["_cstruct"] = cs
+        self.__dict__["_cref"] = ctypes.byref(cs)
+        return cs
+
+    def cref(self):
+        self.c()
+        return self.__dict__["_cref"]
 
     @property
     def total(self) -> int:
@@ -200,60 +226,53 @@ def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle,
                     stream=None) -> int:
     """Returns MOE_OK; eager mode fills handle.host_status (total, flags, data rows)."""
     n = desc.T * desc.k
-    idx_dtype = torch.int64 if desc.idx_is_i64 else torch.int32
-    p_idx = _dev(topk_idx, "topk_idx", idx_dtype, n) if n else None
-    p_w = _dev(topk_w, "topk_w", torch.float32, n, optional=True)
-    p_probs = _dev(multihot_probs, "multihot_probs", torch.float32, desc.T * desc.E, optional=True)
-    hs = handle.host_status
-    if hs.is_cuda or hs.dtype != torch.int32 or hs.numel() < 4:
-        raise MoeError(MOE_ERR_ARG, "host_status must be a host int32 tensor of 4 elements")
-    h = handle.c()
-    return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, ctypes.byref(h),
-                                        hs.data_ptr(), _stream(stream)))
+    p_idx = _dev(topk_idx, "topk_idx", _I64 if desc.idx_is_i64 else _I32, n) if n else None
+    p_w = _dev(topk_w, "topk_w", _F32, n, optional=True)
+    p_probs = _dev(multihot_probs, "multihot_probs", _F32, desc.T * desc.E, optional=True)
+    href = handle.cref()
+    return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, href,
+                                        handle.host_status.data_ptr(), _stream(stream)))
 
 
 def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, rows: torch.Tensor,
                  topk_w: torch.Tensor | None = None, row_w: torch.Tensor | None = None,
                  row_token: torch.Tensor | None = None, row_expert: torch.Tensor | None = None,
                  stream=None) -> int:
-    p_x = _dev(x, "x", torch.bfloat16, desc.T * H) if desc.T else None
-    p_rows = _dev(rows, "rows", torch.bfloat16, R * H) if R else None
-    p_w = _dev(topk_w, "topk_w", torch.float32, desc.T * desc.k, optional=True)
-    p_rw = _dev(row_w, "row_w", torch.float32, R, optional=True)
+    p_x = _dev(x, "x", _BF16, desc.T * H) if desc.T else None
+    p_rows = _dev(rows, "rows", _BF16, R * H) if R else None
+    p_w = _dev(topk_w, "topk_w", _F32, desc.T * desc.k, optional=True)
+    p_rw = _dev(row_w, "row_w", _F32, R, optional=True)
     if desc.T == 0:
         p_w = None
     if R == 0:
         p_rw = None
         if p_w is not None:  # no row to weight; the C ABI pairs the two pointers
             p_w = None
-    p_rt = _dev(row_token, "row_token", torch.int32, R, optional=True)
-    p_re = _dev(row_expert, "row_expert", torch.int32, R, optional=True)
-    h = handle.c()
-    return _check(lib().moe_dispatch(ctypes.byref(desc), ctypes.byref(h), p_x, H, p_w, R, p_rows,
+    p_rt = _dev(row_token, "row_token", _I32, R, optional=True)
+    p_re = _dev(row_expert, "row_expert", _I32, R, optional=True)
+    return _check(lib().moe_dispatch(ctypes.byref(desc), handle.cref(), p_x, H, p_w, R, p_rows,
                                      p_rw, p_rt, p_re, _stream(stream)))
 
 
 def moe_combine(desc: Desc, handle: Handle, Y: torch.Tensor, H: int, R: int, out: torch.Tensor,
                 stream=None) -> int:
     out_f32 = out.dtype == torch.float32
-    p_y = _dev(Y, "Y", torch.bfloat16, R * H) if R else None
+    p_y = _dev(Y, "Y", _BF16, R * H) if R else None
     p_o = _dev(out, "out", (torch.bfloat16, torch.float32), desc.T * H) if desc.T else None
-    h = handle.c()
-    return _check(lib().moe_combine(ctypes.byref(desc), ctypes.byref(h), p_y, H, R, p_o,
+    return _check(lib().moe_combine(ctypes.byref(desc), handle.cref(), p_y, H, R, p_o,
                                     int(out_f32), _stream(stream)))
 
 
 def moe_combine_bwd(desc: Desc, handle: Handle, grad_out: torch.Tensor, H: int, R: int,
                     grad_rows: torch.Tensor, expert_out: torch.Tensor | None = None,
                     dw: torch.Tensor | None = None, stream=None) -> int:
-    p_g = _dev(grad_out, "grad_out", torch.bfloat16, desc.T * H) if desc.T else None
-    p_gr = _dev(grad_rows, "grad_rows", torch.bfloat16, R * H) if R else None
-    p_f = _dev(expert_out, "expert_out", torch.bfloat16, R * H, optional=True) if R else None
-    p_dw = _dev(dw, "dw", torch.float32, desc.T * desc.k, optional=True)
+    p_g = _dev(grad_out, "grad_out", _BF16, desc.T * H) if desc.T else None
+    p_gr = _dev(grad_rows, "grad_rows", _BF16, R * H) if R else None
+    p_f = _dev(expert_out, "expert_out", _BF16, R * H, optional=True) if R else None
+    p_dw = _dev(dw, "dw", _F32, desc.T * desc.k, optional=True)
     if desc.T == 0:  # no slot: nothing for dw to hold, expert_out is not read
         p_f = p_dw = None
-    h = handle.c()
-    return _check(lib().moe_combine_bwd(ctypes.byref(desc), ctypes.byref(h), p_g, p_f, H, R, p_gr,
+    return _check(lib().moe_combine_bwd(ctypes.byref(desc), handle.cref(), p_g, p_f, H, R, p_gr,
                                         p_dw, _stream(stream)))
 
 

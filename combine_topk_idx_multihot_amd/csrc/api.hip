@@ -11,9 +11,12 @@
 #include "moe_mi355x.h"
 #include "moe_internal.h"
 
+#include <immintrin.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
+
+#include <chrono>
 
 namespace {
 
@@ -214,16 +217,30 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    volatile int32_t *hs = host_status;
+    if (a.host_status)
+        hs[3] = -1; // turned to 0 by the kernel once words 0..2 are written
     hipError_t e = moe::launch_route(a, g.threads, s);
     if (e != hipSuccess)
         return hip_fail(e, "route launch");
     if (desc->mode == MOE_EAGER) {
-        // "Eager vs captured": the counts come back to the host once.
-        if (!a.host_status &&
-            (e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
-                                hipMemcpyDeviceToHost, s)) != hipSuccess)
+        // "Eager vs captured": the counts come back to the host once.  With a
+        // device-visible status the host waits only for that word (a bounded
+        // spin, then a stream sync); the rest of the route runs on, ordered
+        // before whatever the caller queues next on the stream.
+        bool ready = false;
+        if (a.host_status) {
+            const auto t0 = std::chrono::steady_clock::now();
+            while (!(ready = (hs[3] == 0))) {
+                _mm_pause();
+                if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(5))
+                    break;
+            }
+        } else if ((e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
+                                       hipMemcpyDeviceToHost, s)) != hipSuccess) {
             return hip_fail(e, "status readback");
-        if ((e = hipStreamSynchronize(s)) != hipSuccess)
+        }
+        if (!ready && (e = hipStreamSynchronize(s)) != hipSuccess)
             return hip_fail(e, "stream sync");
         if (host_status[1] & MOE_FLAG_BAD_ID)
             return fail(MOE_ERR_INDEX, "an expert id outside [-1, E=%d) was seen; such slots were "

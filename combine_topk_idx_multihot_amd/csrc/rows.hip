@@ -31,8 +31,12 @@
 //     wave writes HBM markedly faster than a grid-stride pattern on MI355X.
 //   * combine adds the token's rows in fp32 in ascending slot order (the
 //     accumulator starts from the first row) and writes bf16 (nearest-even)
-//     or fp32; one wave per (token, segment), gather loads non-temporal
-//     (those rows are read once).
+//     or fp32; one wave per (token, segment).
+//   * rows that are written once and not read again by this step (dispatched
+//     rows, grad rows, zeros) use non-temporal stores, and rows read once
+//     (the combine's gather, the backward's expert outputs) non-temporal
+//     loads: measured on MI355X, this keeps the write-back of one kernel from
+//     landing in the next one and shortens the whole step.
 #include "moe_internal.h"
 
 #ifndef MOE_COMBINE_SEG
@@ -49,6 +53,15 @@
 #endif
 #ifndef MOE_NT_ZERO
 #define MOE_NT_ZERO 1
+#endif
+#ifndef MOE_NT_DOT_ROWS
+#define MOE_NT_DOT_ROWS 1
+#endif
+#ifndef MOE_NT_DOT_F
+#define MOE_NT_DOT_F 1
+#endif
+#ifndef MOE_NT_COPY_ROWS
+#define MOE_NT_COPY_ROWS 1
 #endif
 
 
@@ -244,7 +257,8 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
 #pragma unroll
                     for (int b = 0; b < kBatch; ++b)
                         if (b < bt.n)
-                            load_seg<SEG>(f[DOT ? b : 0], a.F, bt.row[b], a.H, c0, nch, lane);
+                            load_seg<SEG, MOE_NT_DOT_F != 0>(f[DOT ? b : 0], a.F, bt.row[b], a.H, c0,
+                                                              nch, lane);
                 }
 #pragma unroll
                 for (int b = 0; b < kBatch; ++b) {
@@ -254,7 +268,7 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
                         for (int i = 0; i < SEG; ++i) {
                             const int c = c0 + i * kWave + lane;
                             if (c < nch)
-                                dst[c] = v[i];
+                                put16<DOT ? MOE_NT_DOT_ROWS != 0 : MOE_NT_COPY_ROWS != 0>(dst + c, v[i]);
                         }
                     }
                 }

@@ -27,8 +27,8 @@
  *   - Return value is a moe_status; on failure moe_last_error() names the
  *     violated requirement.  Argument errors are detected on the host before
  *     anything is launched.  Nothing throws.
- *   - Only MOE_EAGER moe_route_build synchronizes (once, to read the row
- *     count back: "Eager vs captured").  Every other call, and every call in
+ *   - Only MOE_EAGER moe_route_build waits for the device (once, to read the
+ *     row count back: "Eager vs captured").  Every other call, and every call in
  *     MOE_SYNC_FREE mode, is asynchronous, allocation-free and safe to record
  *     into a HIP graph ("Custom ops", "Buffers").
  *   - Calls that share output buffers must not overlap; calls on different
@@ -123,9 +123,12 @@ size_t moe_route_workspace_size(const moe_desc *desc);
  *   handle          outputs (see moe_handle); status is fully rewritten; its
  *                   workspace must hold moe_route_workspace_size bytes.
  *   host_status     host int32[4]: MOE_EAGER receives {total, flags, data rows, 0}
- *                   after the one stream sync.  Pinned memory is written by the
- *                   kernel directly; pageable memory gets a copy after it.
- *                   MOE_SYNC_FREE: unused, may be NULL.
+ *                   before the call returns.  Pinned (device-visible) memory is
+ *                   written by the route kernel directly and the call waits
+ *                   only for that write; the handle's device tensors are then
+ *                   complete in stream order (work queued next on the same
+ *                   stream sees them).  Pageable memory gets a copy and one
+ *                   stream sync.  MOE_SYNC_FREE: unused, may be NULL.
  * Rows inside an expert's group are in ascending token order.  Returns
  * MOE_ERR_INDEX in eager mode when MOE_FLAG_BAD_ID is set (outputs valid).
  */
