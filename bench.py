@@ -279,7 +279,7 @@ def cpu_baseline(wl, st, budget_s, torch):
     C = wl.cap if wl.sync_free else 0
     Y, F = u16(st["Y"]), u16(st["F"])
     reps, t_used, bytes_done = 0, 0.0, 0
-    while t_used < budget_s and reps < 50:
+    while t_used < budget_s and reps < 500:
         t0 = time.perf_counter()
         r = oracle.route(idx, wl.E, wl.lb, EL, wl.P, sync_free=wl.sync_free, C=C, w=w, x=x,
                          want_probs=True)
