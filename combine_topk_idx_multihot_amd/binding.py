@@ -29,7 +29,8 @@ MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
 
 # Every symbol include/moe_mi355x.h declares.
 EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build", "moe_dispatch",
-           "moe_combine", "moe_combine_bwd", "moe_last_error", "moe_device_check")
+           "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd", "moe_last_error",
+           "moe_device_check")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine_bwd.argtypes = [pd, ph, vp, vp, i32, i64, vp, vp, vp]
         L.moe_combine_bwd.restype = ctypes.c_int
+        L.moe_dispatch_bwd.argtypes = [pd, ph, vp, i32, i64, vp, vp, i32, vp, vp]
+        L.moe_dispatch_bwd.restype = ctypes.c_int
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_device_check.argtypes = [ctypes.c_int]
@@ -276,6 +279,22 @@ def moe_combine_bwd(desc: Desc, handle: Handle, grad_out: torch.Tensor, H: int, 
                                         p_dw, _stream(stream)))
 
 
+def moe_dispatch_bwd(desc: Desc, handle: Handle, grad_rows: torch.Tensor, H: int, R: int,
+                     grad_x: torch.Tensor, grad_row_w: torch.Tensor | None = None,
+                     grad_topk_w: torch.Tensor | None = None, stream=None) -> int:
+    f32 = grad_x.dtype == torch.float32
+    p_g = _dev(grad_rows, "grad_rows", _BF16, R * H) if R else None
+    p_x = _dev(grad_x, "grad_x", (torch.bfloat16, torch.float32), desc.T * H) if desc.T else None
+    p_rw = _dev(grad_row_w, "grad_row_w", _F32, R, optional=True) if R else None
+    p_tw = _dev(grad_topk_w, "grad_topk_w", _F32, desc.T * desc.k, optional=True)
+    if desc.T == 0:
+        p_tw = None
+    if p_tw is None:
+        p_rw = None
+    return _check(lib().moe_dispatch_bwd(ctypes.byref(desc), handle.cref(), p_g, H, R, p_rw, p_x,
+                                         int(f32), p_tw, _stream(stream)))
+
+
 def moe_device_check(device: int = 0) -> int:
     return _check(lib().moe_device_check(device))
 
@@ -325,3 +344,14 @@ def combine_bwd(desc: Desc, handle: Handle, grad_out: torch.Tensor, R: int,
     dw = torch.empty((desc.T, desc.k), dtype=torch.float32, device=dev) if expert_out is not None else None
     moe_combine_bwd(desc, handle, grad_out, H, R, grad_rows, expert_out, dw, stream=stream)
     return grad_rows, dw
+
+
+def dispatch_bwd(desc: Desc, handle: Handle, grad_rows: torch.Tensor,
+                 grad_row_w: torch.Tensor | None = None, out_dtype=torch.bfloat16, stream=None):
+    """moe_dispatch_bwd with fresh outputs: (grad_x, grad_topk_w or None)."""
+    R, H = grad_rows.shape
+    gx = torch.empty((desc.T, H), dtype=out_dtype, device=grad_rows.device)
+    gtw = (torch.empty((desc.T, desc.k), dtype=torch.float32, device=grad_rows.device)
+           if grad_row_w is not None else None)
+    moe_dispatch_bwd(desc, handle, grad_rows, H, R, gx, grad_row_w, gtw, stream=stream)
+    return gx, gtw

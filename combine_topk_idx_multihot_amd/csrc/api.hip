@@ -320,6 +320,8 @@ int moe_combine(const moe_desc *desc, const moe_handle *handle, const uint16_t *
     a.Y = Y;
     a.out = out;
     a.row_of_slot = handle->row_of_slot;
+    a.grad_row_w = nullptr;
+    a.grad_w = nullptr;
     a.status = handle->status;
     a.T = desc->T;
     a.R = R;
@@ -380,6 +382,49 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "combine_bwd launch");
+    return ok();
+}
+
+int moe_dispatch_bwd(const moe_desc *desc, const moe_handle *handle, const uint16_t *grad_rows,
+                     int32_t H, int64_t R, const float *grad_row_w, void *grad_x,
+                     int32_t grad_x_is_f32, float *grad_topk_w, void *stream)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if ((rc = check_rows(desc, R)) != MOE_OK)
+        return rc;
+    if (grad_x_is_f32 != 0 && grad_x_is_f32 != 1)
+        return fail(MOE_ERR_ARG, "grad_x_is_f32 must be 0 or 1 (got %d)", grad_x_is_f32);
+    if (R > 0 && (!grad_rows || !aligned16(grad_rows)))
+        return fail(MOE_ERR_ARG, "grad_rows must be a non-NULL, 16-byte aligned [R,H] bf16 tensor");
+    if (desc->T > 0 && (!grad_x || !aligned16(grad_x)))
+        return fail(MOE_ERR_ARG, "grad_x must be a non-NULL, 16-byte aligned [T,H] tensor");
+    if (grad_row_w && !grad_topk_w)
+        return fail(MOE_ERR_ARG, "grad_row_w given but grad_topk_w is NULL (it would be ignored)");
+    if (grad_topk_w && !grad_row_w && R > 0)
+        return fail(MOE_ERR_ARG, "grad_topk_w requested without grad_row_w");
+
+    moe::CombineArgs a;
+    a.Y = grad_rows;
+    a.out = grad_x;
+    a.row_of_slot = handle->row_of_slot;
+    a.grad_row_w = grad_row_w;
+    a.grad_w = grad_topk_w;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.R = R;
+    a.k = desc->k;
+    a.H = H;
+    a.out_f32 = grad_x_is_f32;
+    a.eager = desc->mode == MOE_EAGER;
+    hipError_t e = moe::launch_combine(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "dispatch_bwd launch");
     return ok();
 }
 

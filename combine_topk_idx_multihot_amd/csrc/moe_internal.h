@@ -76,6 +76,8 @@ struct CombineArgs {
     const uint16_t *Y;          // [R,H]
     void *out;                  // [T,H] bf16 or f32
     const int32_t *row_of_slot; // [T,k]
+    const float *grad_row_w;    // [R] or null (dispatch backward: per-row weight gradients)
+    float *grad_w;              // [T,k] or null (dispatch backward: per-slot weight gradients)
     int32_t *status;
     int64_t T, R;
     int32_t k, H;
@@ -83,6 +85,8 @@ struct CombineArgs {
     int32_t eager;
 };
 
+// Combine; with grad_w set it is also the dispatch backward (the weight
+// gradients of the slots are gathered from their rows).
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 
 }  // namespace moe

@@ -393,8 +393,9 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// combine: one wave per (token, segment); the waves of a workgroup read all
-// segments of a token's rows at about the same time
+// combine (and the dispatch backward, which is the same sum plus a gather of
+// the weight gradients): one wave per (token, segment); the waves of a
+// workgroup read all segments of a token's rows at about the same time
 // ---------------------------------------------------------------------------
 template <int SEG, bool OUT_F32>
 __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
@@ -412,6 +413,10 @@ __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
     if (t >= a.T)
         return;
     const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
+    // dispatch backward: a slot's weight gradient is its row's (repeated ids
+    // share the row, whose weight is the plain sum of theirs); 0 without a row
+    if (a.grad_w && c0 == 0 && lane < a.k)
+        a.grad_w[t * a.k + lane] = (sl.valid && a.grad_row_w) ? a.grad_row_w[sl.row] : 0.f;
     float acc[SEG][8];
 #pragma unroll
     for (int i = 0; i < SEG; ++i)

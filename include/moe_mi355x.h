@@ -188,6 +188,25 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
                     const uint16_t *expert_out, int32_t H, int64_t R, uint16_t *grad_rows,
                     float *dw, void *stream);
 
+/*
+ * Dispatch backward ("Training": gradients reach the tokens and the routing
+ * weights, the weight gradients going back through a combine).  The adjoint of
+ * moe_dispatch along the same handle:
+ *   grad_rows    device [R,H] bf16 gradients of the dispatched rows.
+ *   grad_row_w   device [R] fp32 gradients of the dispatched probs (row_w), or
+ *                NULL (then grad_topk_w must be NULL, unless R == 0).
+ *   grad_x       device [T,H] out: the sum of grad_rows over t's distinct local
+ *                slots in ascending slot order, fp32 adds, bf16 RNE
+ *                (grad_x_is_f32 == 0) or fp32; +0 for a token without a local
+ *                slot -- exactly moe_combine of grad_rows.
+ *   grad_topk_w  device [T,k] fp32 out or NULL: grad_row_w of the slot's row for
+ *                every local slot (repeated ids each get their row's value), 0
+ *                for empty or non-local slots.
+ */
+int moe_dispatch_bwd(const moe_desc *desc, const moe_handle *handle, const uint16_t *grad_rows,
+                     int32_t H, int64_t R, const float *grad_row_w, void *grad_x,
+                     int32_t grad_x_is_f32, float *grad_topk_w, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char *moe_last_error(void);
 

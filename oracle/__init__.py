@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_combine_bwd.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, i64, i64,
                                          vp, vp, vp, vp]
         L.oracle_combine_bwd.restype = ctypes.c_int
+        L.oracle_dispatch_bwd.argtypes = [i64, i32, i32, i32, i32, vp, vp, i64, i64, vp, vp, vp,
+                                          vp, vp]
+        L.oracle_dispatch_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -190,3 +193,22 @@ def combine_bwd(idx, row_of_slot, row_token, grad_out, E, lb=0, EL=None, F=None,
     if rc != OK:
         raise ValueError(f"oracle_combine_bwd rc={rc}")
     return gr[:R], dw
+
+
+def dispatch_bwd(idx, row_of_slot, grad_rows, E, lb=0, EL=None, grad_row_w=None, out="bf16"):
+    """Adjoint of dispatch: (grad_x [T,H] bf16 bits or float32, grad_topk_w [T,k] or None)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    ros = np.ascontiguousarray(row_of_slot, dtype=np.int32)
+    G = np.ascontiguousarray(grad_rows, dtype=np.uint16)
+    T, k = idx.shape
+    R, H = G.shape
+    EL = E if EL is None else EL
+    gw = None if grad_row_w is None else np.ascontiguousarray(grad_row_w, dtype=np.float32)
+    ob = np.zeros((T, H), np.uint16) if out == "bf16" else None
+    of = np.zeros((T, H), np.float32) if out == "f32" else None
+    gtw = np.zeros((T, k), np.float32) if gw is not None else None
+    rc = lib().oracle_dispatch_bwd(T, k, E, lb, EL, _p(idx), _p(ros), R, H, _p(G), _p(gw), _p(ob),
+                                   _p(of), _p(gtw))
+    if rc != OK:
+        raise ValueError(f"oracle_dispatch_bwd rc={rc}")
+    return (ob if out == "bf16" else of), gtw

@@ -356,3 +356,38 @@ int oracle_combine_bwd(int64_t T, int32_t k, int32_t E, int32_t lb, int32_t EL,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Dispatch backward ([DEP] "Training": gradients reach the tokens and the    */
+/* routing weights; the weight gradients go back through a combine).          */
+/* ------------------------------------------------------------------------- */
+
+/* Dispatch copies x[t] to the row of each of t's local slots and the slot's
+ * weight to that row's weight (repeated ids: the sum of their weights), so its
+ * adjoint is:
+ *   grad_x[t]         = sum over t's primary local slots, ascending slot, of
+ *                       grad_rows[row]   -- the combine of the grad rows (R9)
+ *   grad_topk_w[t][j] = grad_row_w[row of slot (t,j)] for every local valid
+ *                       slot (a repeated id gets its row's gradient too, since
+ *                       the row's weight is the plain sum of the slots'), and 0
+ *                       for a slot with no local row.
+ * grad_row_w and grad_topk_w may both be NULL. */
+int oracle_dispatch_bwd(int64_t T, int32_t k, int32_t E, int32_t lb, int32_t EL,
+                        const int64_t *idx, const int32_t *row_of_slot, int64_t R, int64_t H,
+                        const uint16_t *grad_rows, const float *grad_row_w,
+                        uint16_t *grad_x_bf16, float *grad_x_f32, float *grad_topk_w)
+{
+    int rc = oracle_combine(T, k, E, lb, EL, idx, row_of_slot, R, H, grad_rows, grad_x_bf16,
+                            grad_x_f32);
+    if (rc != ORC_OK || !grad_topk_w)
+        return rc;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t e = idx[t * k + j];
+            int64_t r = row_of_slot[t * k + j];
+            int local = e >= lb && e < (int64_t)lb + EL && e < E;
+            grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w) ? grad_row_w[r] : 0.0f;
+        }
+    }
+    return ORC_OK;
+}

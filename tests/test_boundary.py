@@ -181,3 +181,20 @@ def test_validation_agrees_with_oracle_argument_rules():
             assert B.lib().moe_route_workspace_size(ctypes.byref(d)) > 0
         else:
             assert route_rc(d, ws_bytes=1 << 30) == want
+
+
+def dbwd_rc(d, H=2048, R=10, g=FAKE, gw=None, gx=FAKE, f32=0, gtw=None):
+    h = _handle()
+    return B.lib().moe_dispatch_bwd(ctypes.byref(d), ctypes.byref(h), g, H, R, gw, gx, f32, gtw,
+                                    None)
+
+
+def test_dispatch_bwd_argument_rules():
+    d = _desc()
+    assert dbwd_rc(d, H=384) == B.MOE_ERR_HIDDEN
+    assert dbwd_rc(d, f32=3) == B.MOE_ERR_ARG
+    assert dbwd_rc(d, g=None) == B.MOE_ERR_ARG
+    assert dbwd_rc(d, gx=FAKE + 2) == B.MOE_ERR_ARG
+    assert dbwd_rc(d, gw=FAKE, gtw=None) == B.MOE_ERR_ARG   # weights given, nowhere to go
+    assert dbwd_rc(d, gw=None, gtw=FAKE) == B.MOE_ERR_ARG   # weight grads without input
+    assert "grad" in B.last_error()

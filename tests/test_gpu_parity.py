@@ -1,5 +1,8 @@
 """GPU parity: the HIP library against the oracle, through the C ABI.
 
+Every case runs route, dispatch, combine, the combine backward (with dw) and
+the dispatch backward (grad_x and the routing-weight gradients).
+
 Routing metadata, permutation, dispatched rows and weights are compared bit for
 bit; combine is expected bit-exact too (same slot order, same rounding) and is
 held at least to 1e-6 relative; dw (exact products, fp64 sums in a different
@@ -92,6 +95,14 @@ class Run:
             torch.cuda.synchronize()
             self.grad_rows = to_np_u16(gr)
             self.dw = dw.cpu().numpy() if dw is not None else None
+        if F is not None:
+            # dispatch backward of (grad rows = F, grad row weights = a ramp)
+            self.grad_row_w = (np.arange(R, dtype=np.float32) * np.float32(0.001) - np.float32(3.0))
+            gx, gtw = B.dispatch_bwd(d, h, to_dev_bf16(F), torch.from_numpy(self.grad_row_w).cuda(),
+                                     out_dtype=torch.float32 if f32_out else torch.bfloat16)
+            torch.cuda.synchronize()
+            self.grad_x = gx.cpu().numpy() if f32_out else to_np_u16(gx)
+            self.grad_topk_w = gtw.cpu().numpy()
 
 
 def check_against_oracle(run, idx, w, x, E, lb=0, EL=None, P=1, sync_free=False, C=0, grad=None,
@@ -129,6 +140,12 @@ def check_against_oracle(run, idx, w, x, E, lb=0, EL=None, P=1, sync_free=False,
         np.testing.assert_array_equal(run.grad_rows, gr)
         if F is not None:
             check_dw(run.dw, dw, idx, ref.row_of_slot, grad, F, lb, EL, E)
+    if F is not None:
+        gx, gtw = oracle.dispatch_bwd(idx, ref.row_of_slot, F, E, lb, EL, grad_row_w=run.grad_row_w,
+                                      out="f32" if f32_out else "bf16")
+        np.testing.assert_array_equal(run.grad_x.view(np.uint32 if f32_out else np.uint16),
+                                      gx.view(np.uint32 if f32_out else np.uint16))
+        np.testing.assert_array_equal(run.grad_topk_w.view(np.uint32), gtw.view(np.uint32))
 
 
 def check_dw(got, ref, idx, row_of_slot, g, F, lb, EL, E, chunk=1024):
@@ -178,9 +195,9 @@ def test_workload_parity_int64_idx_f32_out_expert_rows(name):
     ref = oracle.route(case.idx, wl.E, wl.lb, wl.num_local, wl.P, sync_free=wl.sync_free, C=C)
     Y = inputs.expert_out_rows(ref.R, wl.H, 78)
     run = Run(case.idx, case.w, case.x, wl.E, wl.lb, wl.num_local, wl.P, wl.sync_free, C,
-              idx64=True, f32_out=True, Y=Y)
+              idx64=True, f32_out=True, Y=Y, F=Y)
     check_against_oracle(run, case.idx, case.w, case.x, wl.E, wl.lb, wl.num_local, wl.P,
-                         wl.sync_free, C, f32_out=True, Y=Y)
+                         wl.sync_free, C, f32_out=True, Y=Y, F=Y)
 
 
 # ---------------------------------------------------------------------------

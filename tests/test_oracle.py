@@ -461,3 +461,42 @@ def test_dw_products_are_exact_beyond_fp32_range():
     r = oracle.route(idx, E)
     _, dw = oracle.combine_bwd(idx, r.row_of_slot, r.row_token, torch_bf16(g), E, F=torch_bf16(F))
     assert dw[0, 0] == 1.0
+
+
+# --------------------------------------------------------------------------
+# dispatch backward: the adjoint of dispatch (tokens and routing weights)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_dispatch_bwd_is_the_adjoint_of_dispatch(seed):
+    # <dispatch(x), G> == <x, dispatch_bwd(G)> and <row_w(w), g> == <w, grad_w(g)>,
+    # exact on small-integer data (every sum is exact in fp32 and fp64)
+    rng = np.random.default_rng(600 + seed)
+    T, E, k, H = 40, 10, 4, 256
+    EL, lb, P = (E, 0, 3) if seed % 2 == 0 else (6, 2, 2)
+    sync_free = seed >= 2
+    idx = inputs.random_routing(T, E, k, rng, p_invalid=0.25, allow_dup=(seed % 2 == 1))
+    x = torch_bf16(rng.integers(-4, 5, size=(T, H)).astype(np.float32))
+    w = rng.integers(-3, 4, size=(T, k)).astype(np.float32)
+    C = oracle.capacity_min(T, k, EL, P) if sync_free else 0
+    r = oracle.route(idx, E, lb, EL, P, sync_free=sync_free, C=C, w=w, x=x)
+    G = torch_bf16(rng.integers(-4, 5, size=(r.R, H)).astype(np.float32))
+    g = rng.integers(-3, 4, size=r.R).astype(np.float32)
+    gx, gw = oracle.dispatch_bwd(idx, r.row_of_slot, G, E, lb, EL, grad_row_w=g, out="f32")
+    lhs = float((f32_of_bf16(r.rows).astype(np.float64) * f32_of_bf16(G)).sum())
+    rhs = float((f32_of_bf16(x).astype(np.float64) * gx).sum())
+    assert lhs == rhs
+    assert float((r.row_w.astype(np.float64) * g).sum()) == float((w.astype(np.float64) * gw).sum())
+    # slots without a local row get no weight gradient
+    no_row = r.row_of_slot < 0
+    assert (gw[no_row] == 0).all()
+
+
+def test_dispatch_bwd_inverts_top1_dispatch():
+    rng = np.random.default_rng(8)
+    T, E = 200, 12
+    idx = rng.integers(0, E, size=(T, 1))
+    x = inputs.bf16_normal((T, 512), rng)
+    r = oracle.route(idx, E, P=4, x=x)
+    gx, _ = oracle.dispatch_bwd(idx, r.row_of_slot, r.rows, E)
+    np.testing.assert_array_equal(gx, x)
