@@ -29,15 +29,15 @@ OK, ERR_ARG, ERR_HIDDEN, ERR_CAPACITY, ERR_INDEX = 0, 1, 2, 3, 5
 FLAG_BAD_ID, FLAG_DUP = 1, 2
 
 
-def build() -> str:
+def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile moe_oracle.c into liboracle.so with gcc (strict IEEE: no
     contraction of a*b+c into fma, no fast-math)."""
-    tmp = _LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -46,9 +46,14 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        L = ctypes.CDLL(_LIB)
+        # MOE_ORACLE_LIB: load another build of this source instead (the
+        # planted-mistake test points it at deliberately broken copies)
+        path = os.environ.get("MOE_ORACLE_LIB")
+        if path is None:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        L = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
         L.oracle_bf16_round.argtypes = [ctypes.c_float]
         L.oracle_bf16_round.restype = ctypes.c_uint16

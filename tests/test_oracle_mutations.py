@@ -1,0 +1,55 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case copies oracle/moe_oracle.c, plants one plausible mistake (a dropped
+term, a wrong index or rounding, a reversed order, a wrong constant), builds
+the copy with gcc into a temporary directory and runs tests/test_oracle.py
+against it in a child process.  The pins must fail for every one.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "moe_oracle.c")
+
+MUTATIONS = [
+    ("combine adds a stray term", "acc[h] = have ? acc[h] + v : v;",
+     "acc[h] = have ? acc[h] + v : v + 0.0f * acc[h] + (h == 0 ? 1.0f : 0.0f);"),
+    ("combine drops the last slot", "for (int32_t j = 0; j < k; ++j) {\n            if (!primary_local",
+     "for (int32_t j = 0; j < k - (k > 2); ++j) {\n            if (!primary_local"),
+    ("padding rounds up one too far", "int32_t padded = ((tpe[e] + P - 1) / P) * P;",
+     "int32_t padded = ((tpe[e] + P) / P) * P;"),
+    ("rows in descending token order", "for (int64_t t = 0; t < T; ++t) {\n            if (!map[t * E + lb + e])",
+     "for (int64_t t = T - 1; t >= 0; --t) {\n            if (!map[t * E + lb + e])"),
+    ("repeated ids not merged", "W[t * E + e] = W[t * E + e] + w[t * k + j];", "W[t * E + e] = w[t * k + j];"),
+    ("ties round away from even", "return (lo & 1u) ? hi : lo;", "return hi;"),
+    ("dw products rounded to fp32",
+     "s += bf16_value(grad_out[t * H + h]) * bf16_value(F[r * H + h]);",
+     "s += (float)(bf16_value(grad_out[t * H + h]) * bf16_value(F[r * H + h]));"),
+    ("sentinel expert id wrong", "row_expert[r] = EL;", "row_expert[r] = -1;"),
+    ("no repeated-id check in combine", "for (int32_t q = 0; q < j; ++q)", "for (int32_t q = 0; q < 0; ++q)"),
+    ("slot mapped to the next expert's row", "if (idx[t * k + j] == (int64_t)lb + e)",
+     "if (idx[t * k + j] == (int64_t)lb + e + 1)"),
+    ("counts read one expert over", "c += map[t * E + lb + e];", "c += map[t * E + lb + (e + 1) % EL];"),
+    ("weight gradient of repeated ids dropped",
+     "grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w) ? grad_row_w[r] : 0.0f;",
+     "grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w && (j == 0 || idx[t * k + j - 1] != e)) ? grad_row_w[r] : 0.0f;"),
+]
+
+
+@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(label, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {label}"
+    mutated = tmp_path / "moe_oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.build(str(mutated), str(tmp_path / "liboracle_mut.so"))
+    env = dict(os.environ, MOE_ORACLE_LIB=lib)
+    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle.py"),
+                          "-x", "-q", "-p", "no:cacheprovider"],
+                         env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"the pins did not catch: {label}\n{res.stdout[-2000:]}"
