@@ -158,7 +158,8 @@ class Handle:
     row_of_slot: torch.Tensor          # [T,k] int32
     status: torch.Tensor               # [4] int32 (device)
     host_status: torch.Tensor          # [4] int32 (pinned host)
-    workspace: torch.Tensor            # [moe_route_workspace_size] uint8 (device)
+    workspace: torch.Tensor | None     # [moe_route_workspace_size] uint8 (device); only
+                                       # moe_route_build reads it
 
     def c(self) -> _Handle:
         """The C struct, checked and built once: a Handle's tensors are not to
@@ -167,9 +168,11 @@ class Handle:
         if cs is not None:
             return cs
         d = self.desc
+        ws = self.workspace
         cs = _Handle(
-            workspace=_dev(self.workspace, "workspace", _U8, moe_route_workspace_size(d)),
-            workspace_bytes=self.workspace.numel(),
+            workspace=None if ws is None else _dev(ws, "workspace", _U8,
+                                                   moe_route_workspace_size(d)),
+            workspace_bytes=0 if ws is None else ws.numel(),
             routing_map=_dev(self.routing_map, "routing_map", _U8, d.T * d.E, True),
             tokens_per_expert=_dev(self.tokens_per_expert, "tokens_per_expert", _I32, d.num_local),
             padded_offsets=_dev(self.padded_offsets, "padded_offsets", _I32, d.num_local + 1),

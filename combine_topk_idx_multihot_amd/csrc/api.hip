@@ -102,14 +102,18 @@ WsLayout ws_layout(const moe_desc *d)
     return w;
 }
 
-int check_handle(const moe_desc *d, const moe_handle *h)
+// The workspace is scratch of moe_route_build alone; the calls after it never
+// read it, so only route_build checks it (need_ws).
+int check_handle(const moe_desc *d, const moe_handle *h, bool need_ws = false)
 {
     if (!h)
         return fail(MOE_ERR_ARG, "handle is NULL");
-    const WsLayout wl = ws_layout(d);
-    if (!h->workspace || h->workspace_bytes < wl.bytes)
-        return fail(MOE_ERR_WORKSPACE, "handle.workspace needs %zu bytes (got %zu%s)", wl.bytes,
-                    h->workspace_bytes, h->workspace ? "" : ", NULL");
+    if (need_ws) {
+        const WsLayout wl = ws_layout(d);
+        if (!h->workspace || h->workspace_bytes < wl.bytes)
+            return fail(MOE_ERR_WORKSPACE, "handle.workspace needs %zu bytes (got %zu%s)", wl.bytes,
+                        h->workspace_bytes, h->workspace ? "" : ", NULL");
+    }
     if (!h->tokens_per_expert || !h->padded_offsets || !h->status)
         return fail(MOE_ERR_ARG, "handle tensors tokens_per_expert, padded_offsets and status must be "
                                  "non-NULL");
@@ -169,7 +173,7 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
-    if ((rc = check_handle(desc, handle)) != MOE_OK)
+    if ((rc = check_handle(desc, handle, true)) != MOE_OK)
         return rc;
     if (desc->T > 0 && !topk_idx)
         return fail(MOE_ERR_ARG, "topk_idx is NULL");

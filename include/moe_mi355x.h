@@ -98,7 +98,8 @@ typedef struct moe_handle {
                                    repeated ids point at the first slot's row */
     int32_t *status;            /* [4] {total, flags (MOE_FLAG_*), data rows, 0} */
     void *workspace;            /* >= moe_route_workspace_size(desc) bytes of device
-                                   scratch for moe_route_build (per-block counts) */
+                                   scratch for moe_route_build (per-block counts);
+                                   read by no other call, which accept NULL */
     size_t workspace_bytes;
 } moe_handle;
 

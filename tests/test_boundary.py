@@ -124,9 +124,13 @@ def test_workspace_rules():
     need = B.moe_route_workspace_size(d)
     assert need > 0
     assert route_rc(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+    # only route_build reads the workspace: dispatch gets past the handle check
+    # with none and stops at a later rule (weights with no row_w), launching nothing
     h = _handle(need - 1)
-    assert B.lib().moe_dispatch(ctypes.byref(d), ctypes.byref(h), FAKE, 2048, None, 10, FAKE, None,
-                                None, None, None) == B.MOE_ERR_WORKSPACE
+    h.workspace = None
+    assert B.lib().moe_dispatch(ctypes.byref(d), ctypes.byref(h), FAKE, 2048, FAKE, 10, FAKE, None,
+                                None, None, None) == B.MOE_ERR_ARG
+    assert "row_w" in B.last_error()
     h = _handle()
     h.workspace = None
     assert route_rc(d, handle=h) == B.MOE_ERR_WORKSPACE
