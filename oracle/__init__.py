@@ -77,6 +77,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_dispatch_bwd.argtypes = [i64, i32, i32, i32, i32, vp, vp, i64, i64, vp, vp, vp,
                                           vp, vp]
         L.oracle_dispatch_bwd.restype = ctypes.c_int
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e4m3_round_array.argtypes = [vp, vp, i64]
+        L.oracle_e4m3_round_array.restype = None
+        L.oracle_fp8_quantize_row.argtypes = [i64, vp, vp, vp]
+        L.oracle_fp8_quantize_row.restype = None
+        L.oracle_dispatch_fp8.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+        L.oracle_dispatch_fp8.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -217,3 +225,45 @@ def dispatch_bwd(idx, row_of_slot, grad_rows, E, lb=0, EL=None, grad_row_w=None,
     if rc != OK:
         raise ValueError(f"oracle_dispatch_bwd rc={rc}")
     return (ob if out == "bf16" else of), gtw
+
+
+# ---------------------------------------------------------------------------
+# FP8 dispatch (readings R14..R17 in moe_oracle.c)
+# ---------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 code (NaN for S.1111.111)."""
+    return float(lib().oracle_e4m3_value(int(code) & 0xFF))
+
+
+def e4m3_round(values) -> np.ndarray:
+    """fp32 values -> nearest E4M3 codes (uint8), ties to even, magnitude capped at 448."""
+    v = np.ascontiguousarray(values, dtype=np.float32)
+    out = np.zeros(v.shape, np.uint8)
+    lib().oracle_e4m3_round_array(_p(v), _p(out), v.size)
+    return out
+
+
+def fp8_quantize(x) -> tuple[np.ndarray, np.ndarray]:
+    """Token rows [n,H] (bf16 bits) -> (codes [n,H] uint8, scales [n,H/128] float32)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n, H = x.shape
+    q = np.zeros((n, H), np.uint8)
+    s = np.zeros((n, H // 128), np.float32)
+    for i in range(n):
+        lib().oracle_fp8_quantize_row(H, _p(x[i]), _p(q[i]), _p(s[i]))
+    return q, s
+
+
+def dispatch_fp8(x, row_token) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 rows [R,H] uint8 and scales [R,H/128] for the rows of a routing."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rt = np.ascontiguousarray(row_token, dtype=np.int32)
+    T, H = x.shape
+    R = rt.shape[0]
+    q = np.zeros((max(R, 1), H), np.uint8)
+    s = np.zeros((max(R, 1), H // 128), np.float32)
+    rc = lib().oracle_dispatch_fp8(T, H, _p(x), R, _p(rt), _p(q), _p(s))
+    if rc != OK:
+        raise ValueError(f"oracle_dispatch_fp8 rc={rc}")
+    return q[:R], s[:R]

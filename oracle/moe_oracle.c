@@ -41,6 +41,7 @@
  *   R12 dw is the exact dot product (exact bf16 x bf16 products, fp64 sum in
  *       ascending h), rounded once to fp32;
  *   R13 a token with no primary local slot combines to +0.
+ * The FP8 dispatch (readings R14..R17) is stated at the end of the file.
  */
 #include <math.h>
 #include <stdint.h>
@@ -387,6 +388,109 @@ int oracle_dispatch_bwd(int64_t T, int32_t k, int32_t E, int32_t lb, int32_t EL,
             int64_t r = row_of_slot[t * k + j];
             int local = e >= lb && e < (int64_t)lb + EL && e < E;
             grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w) ? grad_row_w[r] : 0.0f;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* FP8 dispatch ([DEP] "What this adds": FP8 dispatch is named as a follow-up */
+/* to halve the dispatched bytes; the page fixes no format).                  */
+/* ------------------------------------------------------------------------- */
+/*
+ * Readings (R14..R17):
+ *   R14 element format: the OCP 8-bit floating point E4M3 encoding
+ *       ("e4m3fn"): sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *       infinities; S.1111.111 is NaN; largest finite magnitude 448;
+ *       exponent field 0 holds the subnormals m * 2^-9.
+ *   R15 one fp32 scale per token and per 128 consecutive hidden elements:
+ *         a     = max(max_i |x_i|, 1e-4f)
+ *         scale = a / 448            (fp32, nearest-even)
+ *         inv   = 448 / a            (fp32, nearest-even)
+ *         q_i   = e4m3(clamp(x_i * inv, -448, 448))   (fp32 product)
+ *       so that x_i ~= value(q_i) * scale.
+ *   R16 e4m3(v) is the representable value nearest to v, ties to the even
+ *       code (IEEE roundTiesToEven); the sign of v is kept (so -0 -> 0x80).
+ *   R17 pad and sentinel rows are all-zero bytes with scale +0; row weights,
+ *       tokens and experts are those of the bf16 dispatch.
+ * x is expected finite; for NaN or infinite x the result is unspecified.
+ */
+
+/* Value of an E4M3 code, from the field definitions (R14). */
+double oracle_e4m3_value(uint8_t c)
+{
+    int e = (c >> 3) & 15, m = c & 7;
+    double mag = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    if (e == 15 && m == 7)
+        mag = NAN;
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* Nearest E4M3 code (R16) by a scan of the 127 finite non-negative codes:
+ * a later code replaces the best so far if it is strictly nearer, or equally
+ * near and even while the best is odd.  Magnitudes past 448 go to 448. */
+uint8_t oracle_e4m3_round(float f)
+{
+    double v = fabs((double)f);
+    int best = 0;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double dc = fabs(oracle_e4m3_value((uint8_t)c) - v);
+        double db = fabs(oracle_e4m3_value((uint8_t)best) - v);
+        if (dc < db || (dc == db && (c & 1) == 0 && (best & 1) != 0))
+            best = c;
+    }
+    return (uint8_t)((signbit(f) ? 0x80 : 0) | best);
+}
+
+void oracle_e4m3_round_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e4m3_round(in[i]);
+}
+
+/* One token's row x[H] (bf16) -> q[H] (E4M3 codes) and scale[H/128] (R15). */
+void oracle_fp8_quantize_row(int64_t H, const uint16_t *x, uint8_t *q, float *scale)
+{
+    for (int64_t b = 0; b < H / 128; ++b) {
+        const uint16_t *xb = x + b * 128;
+        float amax = 0.0f;
+        for (int i = 0; i < 128; ++i) {
+            float m = fabsf((float)bf16_value(xb[i]));
+            if (m > amax)
+                amax = m;
+        }
+        float a = amax > 1e-4f ? amax : 1e-4f;
+        float s = a / 448.0f;
+        float inv = 448.0f / a;
+        scale[b] = s;
+        for (int i = 0; i < 128; ++i) {
+            float y = (float)bf16_value(xb[i]) * inv;
+            if (y > 448.0f)
+                y = 448.0f;
+            if (y < -448.0f)
+                y = -448.0f;
+            q[b * 128 + i] = oracle_e4m3_round(y);
+        }
+    }
+}
+
+/* The FP8 dispatch of rows [0, R): a data row (row_token[r] >= 0) holds the
+ * quantized row of its token, every other row zero bytes and zero scales
+ * (R17).  row_token is the routing's (oracle_route). */
+int oracle_dispatch_fp8(int64_t T, int64_t H, const uint16_t *x, int64_t R,
+                        const int32_t *row_token, uint8_t *rows_q, float *row_scale)
+{
+    if (oracle_check_hidden(H) != ORC_OK)
+        return ORC_ERR_HIDDEN;
+    const int64_t nb = H / 128;
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t t = row_token[r];
+        if (t >= 0 && t < T) {
+            oracle_fp8_quantize_row(H, x + t * H, rows_q + r * H, row_scale + r * nb);
+        } else {
+            memset(rows_q + r * H, 0, (size_t)H);
+            for (int64_t b = 0; b < nb; ++b)
+                row_scale[r * nb + b] = 0.0f;
         }
     }
     return ORC_OK;

@@ -40,16 +40,32 @@ MUTATIONS = [
      "grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w && (j == 0 || idx[t * k + j - 1] != e)) ? grad_row_w[r] : 0.0f;"),
 ]
 
+# FP8 dispatch, caught by tests/test_oracle_fp8.py
+FP8_MUTATIONS = [
+    ("e4m3 ties to the odd code", "(dc == db && (c & 1) == 0 && (best & 1) != 0)",
+     "(dc == db && (c & 1) != 0)"),
+    ("e4m3 subnormal step halved", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("amax over half the block", "for (int i = 0; i < 128; ++i) {\n            float m",
+     "for (int i = 0; i < 64; ++i) {\n            float m"),
+    ("no floor under amax", "float a = amax > 1e-4f ? amax : 1e-4f;", "float a = amax;"),
+    ("scale inverted", "float s = a / 448.0f;", "float s = 448.0f / a;"),
+    ("pad rows get a nonzero scale", "row_scale[r * nb + b] = 0.0f;", "row_scale[r * nb + b] = 1.0f;"),
+]
 
-@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_is_caught(label, old, new, tmp_path):
+
+CASES = ([m + ("test_oracle.py",) for m in MUTATIONS]
+         + [m + ("test_oracle_fp8.py",) for m in FP8_MUTATIONS])
+
+
+@pytest.mark.parametrize("label,old,new,pins", CASES, ids=[m[0] for m in CASES])
+def test_planted_mistake_is_caught(label, old, new, pins, tmp_path):
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation anchor not found once: {label}"
     mutated = tmp_path / "moe_oracle_mut.c"
     mutated.write_text(src.replace(old, new))
     lib = oracle.build(str(mutated), str(tmp_path / "liboracle_mut.so"))
     env = dict(os.environ, MOE_ORACLE_LIB=lib)
-    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle.py"),
+    res = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, pins),
                           "-x", "-q", "-p", "no:cacheprovider"],
                          env=env, capture_output=True, text=True, timeout=600)
     assert res.returncode != 0, f"the pins did not catch: {label}\n{res.stdout[-2000:]}"
