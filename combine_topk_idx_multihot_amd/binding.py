@@ -29,8 +29,8 @@ MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
 
 # Every symbol include/moe_mi355x.h declares.
 EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build", "moe_dispatch",
-           "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd", "moe_last_error",
-           "moe_device_check")
+           "moe_dispatch_fp8", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
+           "moe_last_error", "moe_device_check")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_build.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp]
         L.moe_dispatch.restype = ctypes.c_int
+        L.moe_dispatch_fp8.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp, vp]
+        L.moe_dispatch_fp8.restype = ctypes.c_int
         L.moe_combine.argtypes = [pd, ph, vp, i32, i64, vp, i32, vp]
         L.moe_combine.restype = ctypes.c_int
         L.moe_combine_bwd.argtypes = [pd, ph, vp, vp, i32, i64, vp, vp, vp]
@@ -260,6 +262,28 @@ def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, ro
                                      p_rw, p_rt, p_re, _stream(stream)))
 
 
+def moe_dispatch_fp8(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int,
+                     rows_q: torch.Tensor, row_scale: torch.Tensor,
+                     topk_w: torch.Tensor | None = None, row_w: torch.Tensor | None = None,
+                     row_token: torch.Tensor | None = None, row_expert: torch.Tensor | None = None,
+                     stream=None) -> int:
+    p_x = _dev(x, "x", _BF16, desc.T * H) if desc.T else None
+    p_q = _dev(rows_q, "rows_q", (torch.uint8, torch.float8_e4m3fn), R * H) if R else None
+    p_s = _dev(row_scale, "row_scale", _F32, R * (H // 128)) if R else None
+    p_w = _dev(topk_w, "topk_w", _F32, desc.T * desc.k, optional=True)
+    p_rw = _dev(row_w, "row_w", _F32, R, optional=True)
+    if desc.T == 0:
+        p_w = None
+    if R == 0:
+        p_rw = None
+        if p_w is not None:
+            p_w = None
+    p_rt = _dev(row_token, "row_token", _I32, R, optional=True)
+    p_re = _dev(row_expert, "row_expert", _I32, R, optional=True)
+    return _check(lib().moe_dispatch_fp8(ctypes.byref(desc), handle.cref(), p_x, H, p_w, R, p_q,
+                                         p_s, p_rw, p_rt, p_re, _stream(stream)))
+
+
 def moe_combine(desc: Desc, handle: Handle, Y: torch.Tensor, H: int, R: int, out: torch.Tensor,
                 stream=None) -> int:
     out_f32 = out.dtype == torch.float32
@@ -331,6 +355,21 @@ def dispatch(desc: Desc, handle: Handle, x: torch.Tensor, topk_w: torch.Tensor |
     re = torch.empty(R, dtype=torch.int32, device=dev) if meta else None
     moe_dispatch(desc, handle, x, H, R, rows, topk_w, row_w, rt, re, stream=stream)
     return rows, row_w, rt, re
+
+
+def dispatch_fp8(desc: Desc, handle: Handle, x: torch.Tensor, topk_w: torch.Tensor | None = None,
+                 meta: bool = True, stream=None):
+    """moe_dispatch_fp8 with fresh outputs: (rows_q [R,H] float8_e4m3fn, row_scale [R,H/128],
+    row_w, row_token, row_expert)."""
+    R, H, dev = rows_for(desc, handle), x.shape[1], x.device
+    rows_q = torch.empty((R, H), dtype=torch.float8_e4m3fn, device=dev)
+    row_scale = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    row_w = torch.empty(R, dtype=torch.float32, device=dev) if topk_w is not None else None
+    rt = torch.empty(R, dtype=torch.int32, device=dev) if meta else None
+    re = torch.empty(R, dtype=torch.int32, device=dev) if meta else None
+    moe_dispatch_fp8(desc, handle, x, H, R, rows_q, row_scale, topk_w, row_w, rt, re,
+                     stream=stream)
+    return rows_q, row_scale, row_w, rt, re
 
 
 def combine(desc: Desc, handle: Handle, Y: torch.Tensor, out_dtype=torch.bfloat16, stream=None):

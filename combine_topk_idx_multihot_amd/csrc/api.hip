@@ -148,6 +148,62 @@ int hip_fail(hipError_t e, const char *what)
 
 
 
+// Argument rules shared by the bf16 and the FP8 dispatch.
+int check_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                   const float *topk_w, int64_t R, const float *row_w)
+{
+    int rc;
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if ((rc = check_handle(desc, handle)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if ((rc = check_rows(desc, R)) != MOE_OK)
+        return rc;
+    if (desc->T > 0 && (!x || !aligned16(x)))
+        return fail(MOE_ERR_ARG, "x must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
+    if (row_w && !topk_w && desc->T > 0)
+        return fail(MOE_ERR_ARG, "row_w requested without topk_w");
+    if (topk_w && !row_w)
+        return fail(MOE_ERR_ARG, "topk_w given but row_w is NULL (the weights would be ignored)");
+    return MOE_OK;
+}
+
+// One launch of the dispatch: bf16 rows, or (rows_q set) E4M3 rows and scales.
+int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                    const float *topk_w, int64_t R, uint16_t *rows, uint8_t *rows_q,
+                    float *row_scale, float *row_w, int32_t *row_token, int32_t *row_expert,
+                    void *stream)
+{
+    moe::RowArgs a;
+    a.src = x;
+    a.topk_w = topk_w;
+    a.F = nullptr;
+    a.rows = rows;
+    a.rows_q = rows_q;
+    a.row_scale = row_scale;
+    a.row_w = row_w;
+    a.row_token = row_token;
+    a.row_expert = row_expert;
+    a.dw = nullptr;
+    a.row_of_slot = handle->row_of_slot;
+    a.tpe = handle->tokens_per_expert;
+    a.off = handle->padded_offsets;
+    a.status = handle->status;
+    a.T = desc->T;
+    a.R = R;
+    a.k = desc->k;
+    a.EL = desc->num_local;
+    a.H = H;
+    a.eager = desc->mode == MOE_EAGER;
+    moe::row_shape(a);
+    hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, rows_q ? "fp8 dispatch launch" : "dispatch launch");
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,47 +314,28 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
                  int32_t *row_expert, void *stream)
 {
     int rc;
-    if ((rc = check_desc(desc)) != MOE_OK)
+    if ((rc = check_dispatch(desc, handle, x, H, topk_w, R, row_w)) != MOE_OK)
         return rc;
-    if ((rc = check_handle(desc, handle)) != MOE_OK)
-        return rc;
-    if ((rc = check_hidden(H)) != MOE_OK)
-        return rc;
-    if ((rc = check_rows(desc, R)) != MOE_OK)
-        return rc;
-    if (desc->T > 0 && (!x || !aligned16(x)))
-        return fail(MOE_ERR_ARG, "x must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
     if (R > 0 && (!rows || !aligned16(rows)))
         return fail(MOE_ERR_ARG, "rows must be a non-NULL, 16-byte aligned [R,H] bf16 tensor");
-    if (row_w && !topk_w && desc->T > 0)
-        return fail(MOE_ERR_ARG, "row_w requested without topk_w");
-    if (topk_w && !row_w)
-        return fail(MOE_ERR_ARG, "topk_w given but row_w is NULL (the weights would be ignored)");
+    return launch_dispatch(desc, handle, x, H, topk_w, R, rows, nullptr, nullptr, row_w, row_token,
+                           row_expert, stream);
+}
 
-    moe::RowArgs a;
-    a.src = x;
-    a.topk_w = topk_w;
-    a.F = nullptr;
-    a.rows = rows;
-    a.row_w = row_w;
-    a.row_token = row_token;
-    a.row_expert = row_expert;
-    a.dw = nullptr;
-    a.row_of_slot = handle->row_of_slot;
-    a.tpe = handle->tokens_per_expert;
-    a.off = handle->padded_offsets;
-    a.status = handle->status;
-    a.T = desc->T;
-    a.R = R;
-    a.k = desc->k;
-    a.EL = desc->num_local;
-    a.H = H;
-    a.eager = desc->mode == MOE_EAGER;
-    moe::row_shape(a);
-    hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return hip_fail(e, "dispatch launch");
-    return ok();
+int moe_dispatch_fp8(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                     const float *topk_w, int64_t R, uint8_t *rows_q, float *row_scale,
+                     float *row_w, int32_t *row_token, int32_t *row_expert, void *stream)
+{
+    int rc;
+    if ((rc = check_dispatch(desc, handle, x, H, topk_w, R, row_w)) != MOE_OK)
+        return rc;
+    if (R > 0 && (!rows_q || !aligned16(rows_q)))
+        return fail(MOE_ERR_ARG, "rows_q must be a non-NULL, 16-byte aligned [R,H] byte tensor");
+    if (R > 0 && (!row_scale || !aligned16(row_scale)))
+        return fail(MOE_ERR_ARG, "row_scale must be a non-NULL, 16-byte aligned [R,H/128] fp32 "
+                                 "tensor");
+    return launch_dispatch(desc, handle, x, H, topk_w, R, nullptr, rows_q, row_scale, row_w,
+                           row_token, row_expert, stream);
 }
 
 int moe_combine(const moe_desc *desc, const moe_handle *handle, const uint16_t *Y, int32_t H,
@@ -368,6 +405,8 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     a.topk_w = nullptr;
     a.F = expert_out;
     a.rows = grad_rows;
+    a.rows_q = nullptr;
+    a.row_scale = nullptr;
     a.row_w = nullptr;
     a.row_token = nullptr;
     a.row_expert = nullptr;

@@ -48,7 +48,9 @@ struct RowArgs {
     const uint16_t *src;       // [T,H] token rows (x or grad_out)
     const float *topk_w;       // [T,k] or null
     const uint16_t *F;         // [R,H] expert outputs for dw, or null
-    uint16_t *rows;            // [R,H]
+    uint16_t *rows;            // [R,H] bf16, or null with rows_q set
+    uint8_t *rows_q;           // [R,H] E4M3 codes (FP8 dispatch) or null
+    float *row_scale;          // [R,H/128] scales of rows_q (FP8 dispatch)
     float *row_w;              // [R] or null
     int32_t *row_token;        // [R] or null
     int32_t *row_expert;       // [R] or null
@@ -65,8 +67,9 @@ struct RowArgs {
     int64_t ntok_blocks, nexp_blocks, nsent_blocks;
 };
 
-// Row movement: dispatch (x -> rows) and the combine backward (grad_out ->
-// grad rows, optional dw), token-major; plus pad / sentinel fill.
+// Row movement: dispatch (x -> rows, or with rows_q set x -> E4M3 rows and
+// block scales) and the combine backward (grad_out -> grad rows, optional
+// dw), token-major; plus pad / sentinel fill.
 // row_shape fills in the launch shape (segment size, waves per token, block
 // counts) from the other fields.
 void row_shape(RowArgs &a);

@@ -63,6 +63,9 @@
 #ifndef MOE_NT_COPY_ROWS
 #define MOE_NT_COPY_ROWS 1
 #endif
+#ifndef MOE_FP8_HW
+#define MOE_FP8_HW 1
+#endif
 
 
 namespace moe {
@@ -71,6 +74,7 @@ constexpr int kBatch = 8;            // rows whose loads are in flight together
 constexpr int64_t kZeroTask = 4096;  // 16-byte chunks (64 KiB) per zero-fill wave task
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -189,6 +193,77 @@ __device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0,
     }
 }
 
+// Zero the 4-byte words [w0, w1) of `base` (16-byte aligned): whole 16-byte
+// chunks as wave tasks, the unaligned head and tail (under 4 words each) by
+// wave 0.
+__device__ __forceinline__ void zero_words(uint32_t *__restrict__ base, int64_t w0, int64_t w1,
+                                           int64_t w, int64_t nw, int lane)
+{
+    if (w1 <= w0)
+        return;
+    const int64_t a0 = (w0 + 3) & ~static_cast<int64_t>(3);
+    const int64_t a1 = w1 & ~static_cast<int64_t>(3);
+    if (a0 >= a1) { // no whole chunk: fewer than 8 words
+        if (w == 0 && lane < w1 - w0)
+            base[w0 + lane] = 0u;
+        return;
+    }
+    if (w == 0) {
+        if (lane < a0 - w0)
+            base[w0 + lane] = 0u;
+        if (lane < w1 - a1)
+            base[a1 + lane] = 0u;
+    }
+    zero_chunks(reinterpret_cast<u32x4 *>(base), a0 >> 2, a1 >> 2, w, nw, lane);
+}
+
+// Zero rows [r0, r1) of the dispatch output: bf16 rows, or E4M3 rows and
+// their scales; `w` of `nw` waves.
+__device__ __forceinline__ void zero_rows(const RowArgs &a, int64_t r0, int64_t r1, int64_t w,
+                                          int64_t nw, int lane)
+{
+    if (a.rows_q) {
+        zero_chunks(reinterpret_cast<u32x4 *>(a.rows_q), r0 * (a.H >> 4), r1 * (a.H >> 4), w, nw,
+                    lane);
+        zero_words(reinterpret_cast<uint32_t *>(a.row_scale), r0 * (a.H >> 7), r1 * (a.H >> 7), w,
+                   nw, lane);
+    } else {
+        zero_chunks(reinterpret_cast<u32x4 *>(a.rows), r0 * (a.H >> 3), r1 * (a.H >> 3), w, nw,
+                    lane);
+    }
+}
+
+// Token and weight of each of the token's rows (dispatch): the row of a
+// repeated id carries the first slot's weight plus the later ones', in slot
+// order.
+__device__ __forceinline__ void write_row_meta(const RowArgs &a, const Slots &sl, int64_t t,
+                                               int lane, bool active)
+{
+    if (!a.row_w && !a.row_token)
+        return;
+    const int k = a.k;
+    const bool prim = sl.valid && sl.first == lane;
+    float W = 0.f;
+    if (a.topk_w && active) {
+        const float myw = lane < k ? a.topk_w[t * k + lane] : 0.f;
+        W = myw;
+        if (sl.dup_mask) {
+            for (int q = 0; q < k; ++q) {
+                const int rq = __builtin_amdgcn_readlane(sl.row, q);
+                const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), q));
+                if (prim && q > lane && rq == sl.row)
+                    W = W + wq;
+            }
+        }
+    }
+    if (prim) {
+        if (a.row_token)
+            a.row_token[sl.row] = static_cast<int32_t>(t);
+        if (a.row_w)
+            a.row_w[sl.row] = W;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // dispatch / combine backward
 // ---------------------------------------------------------------------------
@@ -209,31 +284,10 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
         return;
     const int k = a.k;
     const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, active);
-    const bool prim = sl.valid && sl.first == lane;
 
     // metadata of the token's rows (dispatch only), by the token's first wave
-    if (wt == 0 && (a.row_w || a.row_token)) {
-        float W = 0.f;
-        if (a.topk_w && active) {
-            const float myw = lane < k ? a.topk_w[t * k + lane] : 0.f;
-            W = myw;
-            if (sl.dup_mask) {
-                // repeated ids: the first slot's weight plus the later ones, in slot order
-                for (int q = 0; q < k; ++q) {
-                    const int rq = __builtin_amdgcn_readlane(sl.row, q);
-                    const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), q));
-                    if (prim && q > lane && rq == sl.row)
-                        W = W + wq;
-                }
-            }
-        }
-        if (prim) {
-            if (a.row_token)
-                a.row_token[sl.row] = static_cast<int32_t>(t);
-            if (a.row_w)
-                a.row_w[sl.row] = W;
-        }
-    }
+    if (wt == 0)
+        write_row_meta(a, sl, t, lane, active);
 
     float mydw = 0.f;
     const int nch = a.H >> 3; // 16-byte chunks per row
@@ -345,9 +399,7 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
         if (a.row_w)
             a.row_w[r] = 0.f;
     }
-    const int64_t nch = a.H >> 3;
-    zero_chunks(reinterpret_cast<u32x4 *>(a.rows), pad0 * nch, hi * nch, threadIdx.x / kWave,
-                kRowWaves, tid & (kWave - 1));
+    zero_rows(a, pad0, hi, threadIdx.x / kWave, kRowWaves, tid & (kWave - 1));
 }
 
 // Rows [total, R): zero data, token -1, expert EL (the sentinel), weight 0.
@@ -368,10 +420,8 @@ __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
         if (a.row_w)
             a.row_w[r] = 0.f;
     }
-    const int64_t nch = a.H >> 3;
     const int64_t wave = sb * kRowWaves + (threadIdx.x / kWave);
-    zero_chunks(reinterpret_cast<u32x4 *>(a.rows), r0 * nch, r1 * nch, wave,
-                a.nsent_blocks * kRowWaves, threadIdx.x & (kWave - 1));
+    zero_rows(a, r0, r1, wave, a.nsent_blocks * kRowWaves, threadIdx.x & (kWave - 1));
 }
 
 // Grid: [sentinel blocks][token blocks][expert blocks].  The sentinel tail
@@ -388,6 +438,147 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
     bid -= a.nsent_blocks;
     if (bid < a.ntok_blocks)
         move_token<SEG, DOT>(a, bid);
+    else
+        fill_expert(a, static_cast<int>(bid - a.ntok_blocks));
+}
+
+// ---------------------------------------------------------------------------
+// FP8 dispatch: each token row is quantized once, in 128-element blocks with
+// one fp32 scale each, and the E4M3 codes are written to every one of the
+// token's rows.  A lane holds 8 consecutive elements (one 16-byte chunk of
+// the bf16 row), so a block is 16 consecutive lanes: its amax is a 4-step
+// butterfly inside the 16-lane group, and the lane at the group's start
+// writes the block's scale.  Quantization (one fp32 scale per 128 elements):
+//   a = max(amax, 1e-4), scale = a / 448, q = e4m3(clamp(x * (448 / a))).
+// ---------------------------------------------------------------------------
+constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxFloor = 1e-4f;
+
+// E4M3 code of y (|y| <= 448, not NaN), nearest with ties to even: normal
+// magnitudes keep 3 of the 23 fp32 mantissa bits (round half to even on the
+// 20 dropped bits, a carry moving into the exponent), and the exponent bias
+// moves from 127 to 7; below 2^-6 the code is the count of 2^-9 steps.
+__device__ __forceinline__ uint32_t e4m3_sw(float y)
+{
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t m = u & 0x7FFFFFFFu;
+    uint32_t code;
+    if (m >= 0x3C800000u) // 2^-6
+        code = ((m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    else
+        code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(m) * 512.0f));
+    return sign | code;
+}
+
+// Eight values -> eight E4M3 codes, element i in byte i.
+__device__ __forceinline__ u32x2 e4m3_pack8(const float (&y)[8])
+{
+    u32x2 r;
+#if MOE_FP8_HW
+    // gfx950 converts to the OCP E4M3 format, rounding to nearest even
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+    r[0] = static_cast<uint32_t>(w0);
+    r[1] = static_cast<uint32_t>(w1);
+#else
+    r[0] = e4m3_sw(y[0]) | (e4m3_sw(y[1]) << 8) | (e4m3_sw(y[2]) << 16) | (e4m3_sw(y[3]) << 24);
+    r[1] = e4m3_sw(y[4]) | (e4m3_sw(y[5]) << 8) | (e4m3_sw(y[6]) << 16) | (e4m3_sw(y[7]) << 24);
+#endif
+    return r;
+}
+
+template <int SEG>
+__device__ __forceinline__ void quant_token(const RowArgs &a, int64_t bid)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int nwt = a.waves_per_token;
+    const int tl = wave / nwt;
+    const int wt = wave - tl * nwt;
+    const int64_t t = bid * (kRowWaves / nwt) + tl;
+    if (t >= a.T)
+        return;
+    const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
+    if (wt == 0)
+        write_row_meta(a, sl, t, lane, true);
+    if (!sl.prim_mask)
+        return;
+    const int nch = a.H >> 3; // bf16 chunks of 8 elements per token row
+    const int nb = a.H >> 7;  // scale blocks per row
+    constexpr int SPAN = SEG * kWave;
+    const int nseg = (nch + SPAN - 1) / SPAN;
+    for (int sg = wt; sg < nseg; sg += nwt) {
+        const int c0 = sg * SPAN;
+        u32x4 v[SEG];
+        load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
+        u32x2 q[SEG];
+        float sc[SEG];
+#pragma unroll
+        for (int i = 0; i < SEG; ++i) {
+            const bool in = c0 + i * kWave + lane < nch;
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[2 * j] = in ? bf16_lo(v[i][j]) : 0.f;
+                x[2 * j + 1] = in ? bf16_hi(v[i][j]) : 0.f;
+            }
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                m = fmaxf(m, fabsf(x[j]));
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1)
+                m = fmaxf(m, __shfl_xor(m, o, 16));
+            const float am = fmaxf(m, kAmaxFloor);
+            sc[i] = __fdiv_rn(am, kE4M3Max);
+            const float inv = __fdiv_rn(kE4M3Max, am);
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                y[j] = fminf(fmaxf(x[j] * inv, -kE4M3Max), kE4M3Max);
+            q[i] = e4m3_pack8(y);
+        }
+        uint64_t mrest = sl.prim_mask;
+        while (mrest) {
+            const Batch bt = take_batch(mrest, sl.row);
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (b < bt.n) {
+                    u32x2 *__restrict__ dst = reinterpret_cast<u32x2 *>(a.rows_q + bt.row[b] * a.H);
+                    float *__restrict__ ds = a.row_scale + bt.row[b] * nb;
+#pragma unroll
+                    for (int i = 0; i < SEG; ++i) {
+                        const int c = c0 + i * kWave + lane;
+                        if (c < nch) {
+                            if (MOE_NT_COPY_ROWS)
+                                __builtin_nontemporal_store(q[i], dst + c);
+                            else
+                                dst[c] = q[i];
+                            if ((lane & 15) == 0)
+                                ds[c >> 4] = sc[i];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Grid as k_move_rows: [sentinel blocks][token blocks][expert blocks].
+template <int SEG>
+__global__ void __launch_bounds__(kRowThreads) k_dispatch_fp8(RowArgs a)
+{
+    int64_t bid = blockIdx.x;
+    if (bid < a.nsent_blocks) {
+        fill_sentinel(a, bid);
+        return;
+    }
+    bid -= a.nsent_blocks;
+    if (bid < a.ntok_blocks)
+        quant_token<SEG>(a, bid);
     else
         fill_expert(a, static_cast<int>(bid - a.ntok_blocks));
 }
@@ -493,7 +684,9 @@ static int64_t sentinel_blocks(const RowArgs &a)
         return a.eager ? 1 : 0;
     if (a.eager)
         return 8;
-    const int64_t bytes = a.R * static_cast<int64_t>(a.H) * 2;
+    // bytes per row: bf16 data, or E4M3 codes plus one fp32 scale per 128
+    const int64_t row_bytes = a.rows_q ? a.H + (a.H >> 5) : 2 * static_cast<int64_t>(a.H);
+    const int64_t bytes = a.R * row_bytes;
     const int64_t tasks = (bytes + 65535) / 65536;
     const int64_t nb = (tasks + 4 * kRowWaves - 1) / (4 * kRowWaves);
     return nb < 1 ? 1 : (nb > 4096 ? 4096 : nb);
@@ -529,7 +722,13 @@ hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
     if (nb == 0)
         return hipSuccess;
     const dim3 g(static_cast<unsigned>(nb));
-    if (a.dw)
+    if (a.rows_q) {
+        switch (a.seg) {
+        case 1: k_dispatch_fp8<1><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+        case 2: k_dispatch_fp8<2><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+        default: k_dispatch_fp8<4><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+        }
+    } else if (a.dw)
         launch_move<true>(a.seg, g, a, s);
     else
         launch_move<false>(a.seg, g, a, s);

@@ -159,6 +159,29 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
                  int32_t *row_token, int32_t *row_expert, void *stream);
 
 /*
+ * FP8 dispatch ("What this adds": FP8 dispatch, named there as a follow-up
+ * that halves the dispatched bytes; the page fixes no format, this library
+ * takes the following one).  As moe_dispatch, except that each row holds the
+ * token's row quantized to 8-bit floats:
+ *   rows_q      device [R,H] uint8 out: OCP E4M3 codes ("e4m3fn": bias 7, no
+ *               infinities, largest finite 448).
+ *   row_scale   device [R,H/128] fp32 out: one scale per 128 consecutive
+ *               elements, so that x ~= value(rows_q) * row_scale.
+ * Per token and block of 128 elements:
+ *   a = max(max|x|, 1e-4); scale = a / 448; q = e4m3(clamp(x * (448 / a),
+ *   -448, 448)), each fp32 operation rounded to nearest-even and e4m3()
+ *   the nearest code, ties to even (so a block's largest magnitude maps to
+ *   +-448).  Pad rows and rows >= total are zero bytes with scale 0.
+ * The token is quantized once and its codes written to each of its rows.
+ * x must be finite (for NaN or infinite elements the codes are unspecified).
+ * rows_q and row_scale must be 16-byte aligned; row_w, row_token, row_expert,
+ * errors and flags are those of moe_dispatch.
+ */
+int moe_dispatch_fp8(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                     const float *topk_w, int64_t R, uint8_t *rows_q, float *row_scale,
+                     float *row_w, int32_t *row_token, int32_t *row_expert, void *stream);
+
+/*
  * Combine: out[t] = sum of Y[row] over t's distinct local slots, in ascending
  * slot order, in fp32 (the accumulator starts from the first term).  No
  * weight is applied here: in the expanded layout the experts weight their
