@@ -20,7 +20,8 @@ implementation": distinct layers back to back, median of windows):
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
 (event-timed) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
-host on a bounded sample of the same workload.
+host on a bounded sample of the same workload.  `next` times, outside the
+step, the FP8 dispatch and the dispatch backward on the same routings.
 """
 from __future__ import annotations
 
@@ -56,6 +57,18 @@ def byte_model(wl, tpe_total_valid, R, n_active, idx_bytes, with_probs):
     return {"route": route, "dispatch": dispatch, "combine": combine, "combine_bwd": bwd}
 
 
+def byte_model_next(wl, data_rows, R, n_active):
+    """Algorithmic bytes per launch of the two calls outside the step: the FP8
+    dispatch (codes plus one fp32 scale per 128 elements) and the dispatch
+    backward (the combine of the grad rows plus the weight-gradient gather)."""
+    T, H, k = wl.T, wl.H, wl.k
+    fp8 = (n_active * 2 * H + T * k * 4 * 2
+           + R * H + R * (H // 128) * 4 + R * 12)
+    dbwd = (data_rows * 2 * H + T * k * 4 * 2     # grad rows in, row_of_slot, grad_row_w
+            + T * 2 * H + T * k * 4)               # grad_x out, grad_topk_w out
+    return {"dispatch_fp8": fp8, "dispatch_bwd": dbwd}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -66,6 +79,8 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall budget of the oracle CPU-baseline leg (0 = skip)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip timing the FP8 dispatch and the dispatch backward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 8 plain device-to-device copies of MIB MiB (torch copy_) and "
                          "exit: the reference kernel for scaling HBM traffic counters")
@@ -158,7 +173,8 @@ def main():
         local = (idx >= wl.lb) & (idx < wl.lb + EL)
         n_active = int(local.any(axis=1).sum())
         R = wl.cap if wl.sync_free else int(hs[0])
-        facts.append(byte_model(wl, int(hs[2]), R, n_active, 4, True) | {"R": R})
+        facts.append(byte_model(wl, int(hs[2]), R, n_active, 4, True)
+                     | byte_model_next(wl, int(hs[2]), R, n_active) | {"R": R})
 
     # timed region
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -215,11 +231,63 @@ def main():
     }
 
     result["roofline"]["traffic"] = measured_traffic(wl.name, dominant)
+    if not args.no_next:
+        result["next"] = time_next(wl, d, sets, facts, args.steps, stream, torch, B, kern)
 
     # ---- CPU baseline: the oracle on the host, bounded sample ---------------
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, sets[0], args.cpu_seconds, torch)
     print(json.dumps(result), flush=True)
+
+
+def time_next(wl, d, sets, facts, steps, stream, torch, B, kern):
+    """The FP8 dispatch and the dispatch backward over the same buffer sets
+    (handles as routed by the step), each launch bracketed by HIP events."""
+    H, T, k = wl.H, wl.T, wl.k
+    dev = sets[0]["x"].device
+    gen = torch.Generator(device=dev)
+    for s_i, st in enumerate(sets):
+        R = st["rows"].shape[0]
+        gen.manual_seed(4242 + s_i)
+        st["rows_q"] = torch.empty((R, H), dtype=torch.uint8, device=dev)
+        st["row_scale"] = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+        st["grad_row_w"] = torch.randn(R, generator=gen, device=dev)
+        st["grad_x"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        st["grad_topk_w"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+    def run(i, ev=None):
+        st, f = sets[i % len(sets)], facts[i % len(sets)]
+        R = f["R"]
+        if ev is not None:
+            ev[0].record(stream)
+        B.moe_dispatch_fp8(d, st["h"], st["x"], H, R, st["rows_q"], st["row_scale"], st["w"],
+                           st["row_w"], st["row_token"], st["row_expert"], stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        # grad rows: the F buffer (independent of every other input here)
+        B.moe_dispatch_bwd(d, st["h"], st["F"], H, R, st["grad_x"], st["grad_row_w"],
+                           st["grad_topk_w"], stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(2):
+        run(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    out = {}
+    for j, n in enumerate(("dispatch_fp8", "dispatch_bwd")):
+        ms = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]
+        b = float(np.mean([facts[i % len(sets)][n] for i in range(steps)]))
+        avg = float(np.mean(ms))
+        out[n] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+                  "alg_bytes": int(b), "GBps": round(b / (avg * 1e-3) / 1e9, 1),
+                  "frac_of_peak": round(b / (avg * 1e-3) / 1e9 / PEAK_GBS, 4)}
+    out["dispatch_fp8"]["time_vs_bf16_dispatch"] = round(
+        out["dispatch_fp8"]["avg_us"] / kern["dispatch"]["avg_us"], 3)
+    return out
 
 
 def kernel_source_sha256():

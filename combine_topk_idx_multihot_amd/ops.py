@@ -19,6 +19,10 @@ step runs in the HIP library:
   dispatch(x, topk_w, <handle tensors>, num_experts, local_begin, pad_multiple,
            capacity, R) -> (rows, row_w, row_token, row_expert)
       backward: dispatch_bwd (moe_dispatch_bwd) -> (grad_x, grad_topk_w)
+  dispatch_fp8(same arguments as dispatch)
+      -> (rows_q [R,H] float8_e4m3fn, row_scale [R,H/128], row_w, row_token,
+          row_expert); E4M3 codes with one fp32 scale per 128 elements, no
+      autograd (the codes are a quantization)
   combine(Y, <handle tensors>, num_experts, local_begin, pad_multiple,
           capacity) -> out [T,H] bf16
       backward: combine_bwd (moe_combine_bwd, the cached dispatch of grad_out)
@@ -119,6 +123,36 @@ def dispatch(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tensor,
 def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
       num_experts, local_begin, pad_multiple, capacity, R):
     return (x.new_empty((R, x.shape[1])), x.new_empty(R, dtype=torch.float32),
+            x.new_empty(R, dtype=torch.int32), x.new_empty(R, dtype=torch.int32))
+
+
+@torch.library.custom_op(f"{_NS}::dispatch_fp8", mutates_args=())
+def dispatch_fp8(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tensor,
+                 tokens_per_expert: torch.Tensor, padded_offsets: torch.Tensor,
+                 row_of_slot: torch.Tensor, status: torch.Tensor, num_experts: int,
+                 local_begin: int, pad_multiple: int, capacity: int, R: int
+                 ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    """FP8 dispatch: (rows_q [R,H] float8_e4m3fn, row_scale [R,H/128] fp32, row_w,
+    row_token, row_expert).  Not differentiable (the codes are a quantization)."""
+    desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
+                       num_experts, local_begin, pad_multiple, capacity)
+    H = x.shape[1]
+    rows_q = x.new_empty((R, H), dtype=torch.float8_e4m3fn)
+    row_scale = x.new_empty((R, H // 128), dtype=torch.float32)
+    row_w = x.new_empty(R, dtype=torch.float32)
+    row_token = x.new_empty(R, dtype=torch.int32)
+    row_expert = x.new_empty(R, dtype=torch.int32)
+    B.moe_dispatch_fp8(desc, h, x.contiguous(), H, R, rows_q, row_scale, topk_w.contiguous(),
+                       row_w, row_token, row_expert)
+    return rows_q, row_scale, row_w, row_token, row_expert
+
+
+@dispatch_fp8.register_fake
+def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
+      num_experts, local_begin, pad_multiple, capacity, R):
+    H = x.shape[1]
+    return (x.new_empty((R, H), dtype=torch.float8_e4m3fn),
+            x.new_empty((R, H // 128), dtype=torch.float32), x.new_empty(R, dtype=torch.float32),
             x.new_empty(R, dtype=torch.int32), x.new_empty(R, dtype=torch.int32))
 
 

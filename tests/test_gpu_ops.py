@@ -188,3 +188,22 @@ def test_opcheck():
     torch.library.opcheck(ops.dispatch, args)
     rows = ops.dispatch(*args)[0].detach().requires_grad_(True)
     torch.library.opcheck(ops.combine, (rows,) + tuple(meta[:5]) + (c.E, c.lb, c.P, c.C))
+
+
+def test_fp8_dispatch_op_matches_oracle():
+    c = Case(T=333, k=4, E=24, lb=4, EL=16, P=4, H=768, seed=61, sync_free=True)
+    say("ops dispatch_fp8 (sync-free, H=768)")
+    x, idx, w, _, _ = c.device_inputs()
+    meta = ops.route(idx, c.E, c.lb, c.EL, c.P, c.C)
+    q, s, rw, rt, re = ops.dispatch_fp8(x.detach(), w.detach(), *meta[:5], c.E, c.lb, c.P, c.C,
+                                        c.C)
+    torch.cuda.synchronize()
+    ref = oracle.route(c.idx, c.E, c.lb, c.EL, c.P, sync_free=True, C=c.C, w=c.w)
+    rq, rs = oracle.dispatch_fp8(c.x, ref.row_token)
+    np.testing.assert_array_equal(q.view(torch.uint8).cpu().numpy(), rq)
+    np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+    np.testing.assert_array_equal(rt.cpu().numpy(), ref.row_token)
+    np.testing.assert_array_equal(re.cpu().numpy(), ref.row_expert)
+    args = (x.detach(), w.detach()) + tuple(meta[:5]) + (c.E, c.lb, c.P, c.C, c.C)
+    torch.library.opcheck(ops.dispatch_fp8, args)

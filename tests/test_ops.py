@@ -6,7 +6,7 @@ from torch.fx.experimental.proxy_tensor import make_fx
 
 from combine_topk_idx_multihot_amd import ops
 
-OPS = ("route", "dispatch", "dispatch_bwd", "combine", "combine_bwd")
+OPS = ("route", "dispatch", "dispatch_fp8", "dispatch_bwd", "combine", "combine_bwd")
 
 
 def test_ops_are_registered():
@@ -31,6 +31,10 @@ def test_fake_shapes():
         assert rows.shape == (C, H) and rows.dtype == torch.bfloat16
         assert row_w.shape == rt.shape == re.shape == (C,)
         assert row_w.dtype == torch.float32 and rt.dtype == re.dtype == torch.int32
+        q, sc, qw, qt, qe = ops.dispatch_fp8(x, w, *meta[:5], E, 16, P, C, C)
+        assert q.shape == (C, H) and q.dtype == torch.float8_e4m3fn
+        assert sc.shape == (C, H // 128) and sc.dtype == torch.float32
+        assert qw.shape == qt.shape == qe.shape == (C,)
         out = ops.combine(rows, *meta[:5], E, 16, P, C)
         assert out.shape == (T, H) and out.dtype == torch.bfloat16
         gr = ops.combine_bwd(out, C, *meta[:5], E, 16, P, C)
