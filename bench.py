@@ -6,7 +6,7 @@ One step = one pass of the whole path over one layer's batch:
   (cached dispatch of grad_out plus the routing-weight gradients).
 
 Protocol (after the benchmark section of "Add the deepep expert-parallel
-implementation": distinct layers back to back, median of windows):
+implementation": distinct layers back to back):
   * `--sets` (default 4) independent layer buffer sets, each with its own
     routing, rotated step by step so a step's inputs were last touched several
     hundred MB of traffic earlier (MI355X's 256 MB Infinity Cache);
@@ -14,8 +14,11 @@ implementation": distinct layers back to back, median of windows):
     GEMM output) and the backward reads another one, F (the expert output
     before the routing weight), so no kernel of a step re-reads what an
     earlier kernel of the same step left in cache;
-  * W warm-up steps, then K timed steps between two device synchronizations;
-    each kernel is also bracketed by HIP events on the launch stream.
+  * W warm-up steps; K untimed steps with every kernel bracketed by HIP
+    events (the per-kernel breakdown, which picks the dominant kernel); then
+    the timed region: K steps between two device synchronizations, with only
+    the dominant kernel bracketed by events on its launch stream (an event
+    between every pair of kernels costs the step a few µs each).
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
@@ -138,25 +141,27 @@ def main():
 
     names = ("route", "dispatch", "combine", "combine_bwd")
 
-    def step(st, events=None):
-        ev = events
-        if ev is not None:
-            ev[0].record(stream)
+    def step(st, marks=None):
+        """One pass of the path; marks = {boundary: event} records events at
+        kernel boundaries 0 (before route) .. 4 (after combine_bwd)."""
+        m = marks or {}
+        if 0 in m:
+            m[0].record(stream)
         B.moe_route_build(d, st["idx"], st["h"], st["w"], st["probs"], stream=stream)
         R = wl.cap if wl.sync_free else st["h"].total
-        if ev is not None:
-            ev[1].record(stream)
+        if 1 in m:
+            m[1].record(stream)
         B.moe_dispatch(d, st["h"], st["x"], H, R, st["rows"], st["w"], st["row_w"],
                        st["row_token"], st["row_expert"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        if 2 in m:
+            m[2].record(stream)
         B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
+        if 3 in m:
+            m[3].record(stream)
         B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["F"], st["dw"],
                           stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
+        if 4 in m:
+            m[4].record(stream)
         return R
 
     for i in range(args.warmup):
@@ -176,32 +181,40 @@ def main():
         facts.append(byte_model(wl, int(hs[2]), R, n_active, 4, True)
                      | byte_model_next(wl, int(hs[2]), R, n_active) | {"R": R})
 
-    # timed region
+    # breakdown pass (untimed): every kernel bracketed by events; picks the
+    # dominant kernel.  Events between all kernels cost the step a few µs
+    # each, so the timed region below brackets only the dominant one.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(sets[i % len(sets)], dict(enumerate(evs[i])))
+    torch.cuda.synchronize()
+    kern = {}
+    for j, n in enumerate(names):
+        ms = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+        b = float(np.mean([facts[i % len(sets)][n] for i in range(args.steps)]))
+        avg = float(np.mean(ms))
+        kern[n] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
+                   "alg_bytes": int(b), "GBps": round(b / (avg * 1e-3) / 1e9, 1)}
+    dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda n: kern[n]["avg_us"])
+    jd = names.index(dominant)
+
+    # timed region: K steps between two synchronizations; the dominant
+    # kernel's launches bracketed by events on the launch stream
+    dev_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % len(sets)], evs[i])
+        step(sets[i % len(sets)], {jd: dev_[i][0], jd + 1: dev_[i][1]})
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-
-    per_kernel_ms = {n: [] for n in names}
-    bytes_sum = {n: 0 for n in names}
-    for i in range(args.steps):
-        f = facts[i % len(sets)]
-        for j, n in enumerate(names):
-            per_kernel_ms[n].append(evs[i][j].elapsed_time(evs[i][j + 1]))
-            bytes_sum[n] += f[n]
-    kern = {}
-    for n in names:
-        avg_ms = float(np.mean(per_kernel_ms[n]))
-        avg_bytes = bytes_sum[n] / args.steps
-        kern[n] = {"avg_us": round(avg_ms * 1e3, 2), "median_us": round(float(np.median(per_kernel_ms[n])) * 1e3, 2),
-                   "alg_bytes": int(avg_bytes), "GBps": round(avg_bytes / (avg_ms * 1e-3) / 1e9, 1)}
-    step_bytes = sum(bytes_sum.values()) / args.steps
+    step_bytes = float(np.mean([sum(facts[i % len(sets)][n] for n in names)
+                                for i in range(args.steps)]))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda n: kern[n]["avg_us"])
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_]))
+    dom_bytes = float(np.mean([facts[i % len(sets)][dominant] for i in range(args.steps)]))
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     dev_us = sum(kern[n]["avg_us"] for n in names)
 
     result = {
@@ -225,9 +238,10 @@ def main():
                          "backward_device": kern["combine_bwd"]["avg_us"],
                          "step_wall": round(ms_per_step * 1e3, 2), "step_device": round(dev_us, 2)},
         "kernels": kern,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": kern[dominant]["GBps"],
-                     "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kern[dominant]["GBps"] / PEAK_GBS, 4), "traffic": None},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),
+                     "traffic": None, "avg_us": round(dom_ms * 1e3, 2),
+                     "alg_bytes_per_launch": int(dom_bytes)},
     }
 
     result["roofline"]["traffic"] = measured_traffic(wl.name, dominant)

@@ -144,7 +144,8 @@ _U8, _I32, _I64, _F32, _BF16 = ((torch.uint8,), (torch.int32,), (torch.int64,), 
 
 def _stream(stream) -> int:
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        # the current stream of the current device, without building a Stream object
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -191,14 +192,20 @@ class Handle:
         self.c()
         return self.__dict__["_cref"]
 
+    def _host_words(self):
+        hw = self.__dict__.get("_host_np")
+        if hw is None:
+            hw = self.__dict__["_host_np"] = self.host_status.numpy()
+        return hw
+
     @property
     def total(self) -> int:
         """Padded row total from the last eager moe_route_build."""
-        return int(self.host_status[0])
+        return int(self._host_words()[0])
 
     @property
     def flags(self) -> int:
-        return int(self.host_status[1])
+        return int(self._host_words()[1])
 
 
 def alloc_handle(desc: Desc, device="cuda", with_map: bool = True) -> Handle:

@@ -20,7 +20,7 @@
 //     per wave), and a token's segments are dealt over 1, 2 or 4 waves of the
 //     workgroup, so that even a few thousand tokens keep enough waves (and
 //     bytes) in flight on 256 CUs.  Within a segment a wave issues the loads
-//     of up to kBatch rows before consuming any of them.
+//     of up to 8 rows before consuming any of them.
 //   * the combine backward is the dispatch of grad_out plus the expert-output
 //     rows of the token's slots, reduced to fp64 dots: per lane over its
 //     segments, across the wave by butterfly, across the token's waves in LDS
@@ -66,11 +66,24 @@
 #ifndef MOE_FP8_HW
 #define MOE_FP8_HW 1
 #endif
+#ifndef MOE_COPY_BATCH
+#define MOE_COPY_BATCH 8
+#endif
+#ifndef MOE_DOT_BATCH
+#define MOE_DOT_BATCH 8
+#endif
+#ifndef MOE_COMBINE_BATCH
+#define MOE_COMBINE_BATCH 8
+#endif
 
 
 namespace moe {
 
-constexpr int kBatch = 8;            // rows whose loads are in flight together
+// rows whose loads (or stores) a wave keeps in flight together: dispatch and
+// FP8 dispatch (stores), the combine backward (loads of expert rows), combine
+constexpr int kCopyBatch = MOE_COPY_BATCH;
+constexpr int kDotBatch = MOE_DOT_BATCH;
+constexpr int kCombBatch = MOE_COMBINE_BATCH;
 constexpr int64_t kZeroTask = 4096;  // 16-byte chunks (64 KiB) per zero-fill wave task
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -126,20 +139,22 @@ __device__ __forceinline__ Slots load_slots(const int32_t *__restrict__ row_of_s
     return s;
 }
 
-// Up to kBatch slots taken (ascending) off a lane mask: their lanes and rows
+// Up to NB slots taken (ascending) off a lane mask: their lanes and rows
 // (wave-uniform values).
+template <int NB>
 struct Batch {
     int n;
-    int lane[kBatch];
-    int64_t row[kBatch];
+    int lane[NB];
+    int64_t row[NB];
 };
 
-__device__ __forceinline__ Batch take_batch(uint64_t &m, int row)
+template <int NB>
+__device__ __forceinline__ Batch<NB> take_batch(uint64_t &m, int row)
 {
-    Batch bt;
+    Batch<NB> bt;
     bt.n = 0;
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
+    for (int b = 0; b < NB; ++b) {
         bt.lane[b] = 0;
         bt.row[b] = 0;
         if (m) {
@@ -270,7 +285,8 @@ __device__ __forceinline__ void write_row_meta(const RowArgs &a, const Slots &sl
 template <int SEG, bool DOT>
 __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
 {
-    __shared__ double red[kRowWaves][kBatch]; // per-wave dot partials (DOT)
+    constexpr int NB = DOT ? kDotBatch : kCopyBatch;
+    __shared__ double red[kRowWaves][NB]; // per-wave dot partials (DOT)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nwt = a.waves_per_token;
@@ -293,29 +309,29 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
     const int nch = a.H >> 3; // 16-byte chunks per row
     constexpr int SPAN = SEG * kWave;
     const int nseg = (nch + SPAN - 1) / SPAN;
-    const int rounds = DOT ? (k + kBatch - 1) / kBatch : 0;
+    const int rounds = DOT ? (k + NB - 1) / NB : 0;
     uint64_t mrest = sl.prim_mask;
     for (int ib = 0; DOT ? ib < rounds : mrest != 0; ++ib) {
-        const Batch bt = take_batch(mrest, sl.row);
-        double part[kBatch];
+        const Batch<NB> bt = take_batch<NB>(mrest, sl.row);
+        double part[NB];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b)
+        for (int b = 0; b < NB; ++b)
             part[b] = 0.0;
         if (bt.n > 0) {
             for (int sg = wt; sg < nseg; sg += nwt) {
                 const int c0 = sg * SPAN;
                 u32x4 v[SEG];
                 load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
-                u32x4 f[DOT ? kBatch : 1][SEG];
+                u32x4 f[DOT ? NB : 1][SEG];
                 if (DOT) {
 #pragma unroll
-                    for (int b = 0; b < kBatch; ++b)
+                    for (int b = 0; b < NB; ++b)
                         if (b < bt.n)
                             load_seg<SEG, MOE_NT_DOT_F != 0>(f[DOT ? b : 0], a.F, bt.row[b], a.H, c0,
                                                               nch, lane);
                 }
 #pragma unroll
-                for (int b = 0; b < kBatch; ++b) {
+                for (int b = 0; b < NB; ++b) {
                     if (b < bt.n) {
                         u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + bt.row[b] * a.H);
 #pragma unroll
@@ -328,7 +344,7 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
                 }
                 if (DOT) {
 #pragma unroll
-                    for (int b = 0; b < kBatch; ++b) {
+                    for (int b = 0; b < NB; ++b) {
                         if (b < bt.n) {
 #pragma unroll
                             for (int i = 0; i < SEG; ++i) {
@@ -351,7 +367,7 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
         }
         if (DOT) {
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 if (b < bt.n) {
                     double s = part[b];
 #pragma unroll
@@ -364,7 +380,7 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
             __syncthreads();
             if (wt == 0) {
 #pragma unroll
-                for (int b = 0; b < kBatch; ++b) {
+                for (int b = 0; b < NB; ++b) {
                     if (b < bt.n) {
                         double s = red[wave][b];
                         for (int w = 1; w < nwt; ++w)
@@ -543,9 +559,9 @@ __device__ __forceinline__ void quant_token(const RowArgs &a, int64_t bid)
         }
         uint64_t mrest = sl.prim_mask;
         while (mrest) {
-            const Batch bt = take_batch(mrest, sl.row);
+            const Batch<kCopyBatch> bt = take_batch<kCopyBatch>(mrest, sl.row);
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
+            for (int b = 0; b < kCopyBatch; ++b) {
                 if (b < bt.n) {
                     u32x2 *__restrict__ dst = reinterpret_cast<u32x2 *>(a.rows_q + bt.row[b] * a.H);
                     float *__restrict__ ds = a.row_scale + bt.row[b] * nb;
@@ -617,14 +633,14 @@ __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
     bool first = true;
     uint64_t mrest = sl.prim_mask;
     while (mrest) {
-        const Batch bt = take_batch(mrest, sl.row);
-        u32x4 f[kBatch][SEG];
+        const Batch<kCombBatch> bt = take_batch<kCombBatch>(mrest, sl.row);
+        u32x4 f[kCombBatch][SEG];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b)
+        for (int b = 0; b < kCombBatch; ++b)
             if (b < bt.n)
                 load_seg<SEG, true>(f[b], a.Y, bt.row[b], a.H, c0, nch, lane);
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
+        for (int b = 0; b < kCombBatch; ++b) {
             if (b < bt.n) {
 #pragma unroll
                 for (int i = 0; i < SEG; ++i) {
