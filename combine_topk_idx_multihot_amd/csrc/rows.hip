@@ -20,11 +20,14 @@
 //     per wave), and a token's segments are dealt over 1, 2 or 4 waves of the
 //     workgroup, so that even a few thousand tokens keep enough waves (and
 //     bytes) in flight on 256 CUs.  Within a segment a wave issues the loads
-//     of up to 8 rows before consuming any of them.
-//   * the combine backward is the dispatch of grad_out plus the expert-output
-//     rows of the token's slots, reduced to fp64 dots: per lane over its
-//     segments, across the wave by butterfly, across the token's waves in LDS
-//     in a fixed order, so dw is the same on every run.
+//     of a batch of rows (8 for combine, 4 for the dots) before consuming any
+//     of them.
+//   * the combine backward is the dispatch of grad_out plus, in workgroups of
+//     their own interleaved with the copying ones, the fp64 dots of grad_out
+//     with the expert-output rows of the token's slots: one wave per token
+//     walks the row and keeps its partial dots in registers, a butterfly
+//     over the wave ends each dot, so dw is the same on every run and no
+//     wave waits for another.
 //   * pad rows (one workgroup per expert) and the sentinel tail [total, R)
 //     are zeroed by extra workgroups of the same launch.  The tail is one
 //     contiguous range, cut into 64 KiB wave tasks: a contiguous stream per
@@ -42,9 +45,6 @@
 #ifndef MOE_COMBINE_SEG
 #define MOE_COMBINE_SEG 2
 #endif
-#ifndef MOE_BWD_SEG
-#define MOE_BWD_SEG 2
-#endif
 #ifndef MOE_COPY_SEG
 #define MOE_COPY_SEG 2
 #endif
@@ -53,9 +53,6 @@
 #endif
 #ifndef MOE_NT_ZERO
 #define MOE_NT_ZERO 1
-#endif
-#ifndef MOE_NT_DOT_ROWS
-#define MOE_NT_DOT_ROWS 1
 #endif
 #ifndef MOE_NT_DOT_F
 #define MOE_NT_DOT_F 1
@@ -66,11 +63,14 @@
 #ifndef MOE_FP8_HW
 #define MOE_FP8_HW 1
 #endif
+#ifndef MOE_DOT_SEG
+#define MOE_DOT_SEG 2
+#endif
 #ifndef MOE_COPY_BATCH
 #define MOE_COPY_BATCH 8
 #endif
 #ifndef MOE_DOT_BATCH
-#define MOE_DOT_BATCH 8
+#define MOE_DOT_BATCH 4
 #endif
 #ifndef MOE_COMBINE_BATCH
 #define MOE_COMBINE_BATCH 8
@@ -280,121 +280,52 @@ __device__ __forceinline__ void write_row_meta(const RowArgs &a, const Slots &sl
 }
 
 // ---------------------------------------------------------------------------
-// dispatch / combine backward
+// dispatch (x -> rows) and the grad rows of the combine backward (grad_out ->
+// rows): a token's row read once, written to each of its local rows
 // ---------------------------------------------------------------------------
-template <int SEG, bool DOT>
+template <int SEG>
 __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
 {
-    constexpr int NB = DOT ? kDotBatch : kCopyBatch;
-    __shared__ double red[kRowWaves][NB]; // per-wave dot partials (DOT)
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nwt = a.waves_per_token;
     const int tl = wave / nwt;        // token of this wave inside the workgroup
     const int wt = wave - tl * nwt;   // this wave's share of the token's segments
     const int64_t t = bid * (kRowWaves / nwt) + tl;
-    const bool active = t < a.T;
-    // DOT uses workgroup barriers, so every wave runs the same number of
-    // batch rounds, active or not; without DOT idle waves just leave.
-    if (!DOT && !active)
+    if (t >= a.T)
         return;
-    const int k = a.k;
-    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, active);
+    const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
 
     // metadata of the token's rows (dispatch only), by the token's first wave
     if (wt == 0)
-        write_row_meta(a, sl, t, lane, active);
+        write_row_meta(a, sl, t, lane, true);
 
-    float mydw = 0.f;
     const int nch = a.H >> 3; // 16-byte chunks per row
     constexpr int SPAN = SEG * kWave;
     const int nseg = (nch + SPAN - 1) / SPAN;
-    const int rounds = DOT ? (k + NB - 1) / NB : 0;
-    uint64_t mrest = sl.prim_mask;
-    for (int ib = 0; DOT ? ib < rounds : mrest != 0; ++ib) {
-        const Batch<NB> bt = take_batch<NB>(mrest, sl.row);
-        double part[NB];
+    if (!sl.prim_mask)
+        return;
+    for (int sg = wt; sg < nseg; sg += nwt) {
+        const int c0 = sg * SPAN;
+        u32x4 v[SEG];
+        load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
+        uint64_t mrest = sl.prim_mask;
+        while (mrest) {
+            const Batch<kCopyBatch> bt = take_batch<kCopyBatch>(mrest, sl.row);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-            part[b] = 0.0;
-        if (bt.n > 0) {
-            for (int sg = wt; sg < nseg; sg += nwt) {
-                const int c0 = sg * SPAN;
-                u32x4 v[SEG];
-                load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
-                u32x4 f[DOT ? NB : 1][SEG];
-                if (DOT) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        if (b < bt.n)
-                            load_seg<SEG, MOE_NT_DOT_F != 0>(f[DOT ? b : 0], a.F, bt.row[b], a.H, c0,
-                                                              nch, lane);
-                }
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < bt.n) {
-                        u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + bt.row[b] * a.H);
-#pragma unroll
-                        for (int i = 0; i < SEG; ++i) {
-                            const int c = c0 + i * kWave + lane;
-                            if (c < nch)
-                                put16<DOT ? MOE_NT_DOT_ROWS != 0 : MOE_NT_COPY_ROWS != 0>(dst + c, v[i]);
-                        }
-                    }
-                }
-                if (DOT) {
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        if (b < bt.n) {
-#pragma unroll
-                            for (int i = 0; i < SEG; ++i) {
-                                const int c = c0 + i * kWave + lane;
-                                if (c < nch) {
-#pragma unroll
-                                    for (int q = 0; q < 4; ++q) {
-                                        const uint32_t gw = v[i][q], fw = f[DOT ? b : 0][i][q];
-                                        part[b] = fma(static_cast<double>(bf16_lo(gw)),
-                                                      static_cast<double>(bf16_lo(fw)), part[b]);
-                                        part[b] = fma(static_cast<double>(bf16_hi(gw)),
-                                                      static_cast<double>(bf16_hi(fw)), part[b]);
-                                    }
-                                }
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        if (DOT) {
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
+            for (int b = 0; b < kCopyBatch; ++b) {
                 if (b < bt.n) {
-                    double s = part[b];
+                    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + bt.row[b] * a.H);
 #pragma unroll
-                    for (int o = kWave / 2; o >= 1; o >>= 1)
-                        s += __shfl_xor(s, o);
-                    if (lane == 0)
-                        red[wave][b] = s;
-                }
-            }
-            __syncthreads();
-            if (wt == 0) {
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (b < bt.n) {
-                        double s = red[wave][b];
-                        for (int w = 1; w < nwt; ++w)
-                            s += red[wave + w][b];
-                        if (sl.valid && sl.first == bt.lane[b])
-                            mydw = static_cast<float>(s);
+                    for (int i = 0; i < SEG; ++i) {
+                        const int c = c0 + i * kWave + lane;
+                        if (c < nch)
+                            put16<MOE_NT_COPY_ROWS != 0>(dst + c, v[i]);
                     }
                 }
             }
-            __syncthreads();
         }
     }
-    if (DOT && a.dw && active && wt == 0 && lane < k)
-        a.dw[t * k + lane] = sl.valid ? mydw : 0.f;
 }
 
 // Pad rows of one expert's group: zero data, token -1, weight 0; every row of
@@ -443,7 +374,7 @@ __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
 // Grid: [sentinel blocks][token blocks][expert blocks].  The sentinel tail
 // (all of the worst-case rows past total) is the longest-running part in
 // sync-free mode, so its workgroups are dispatched first.
-template <int SEG, bool DOT>
+template <int SEG>
 __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 {
     int64_t bid = blockIdx.x;
@@ -453,9 +384,107 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
     }
     bid -= a.nsent_blocks;
     if (bid < a.ntok_blocks)
-        move_token<SEG, DOT>(a, bid);
+        move_token<SEG>(a, bid);
     else
         fill_expert(a, static_cast<int>(bid - a.ntok_blocks));
+}
+
+// ---------------------------------------------------------------------------
+// combine backward, split form: the grad rows are a plain dispatch of
+// grad_out (move_token without dots), and dw comes from separate waves that
+// each own one token: the token's row is walked in segments of SEG chunks
+// per lane, the fp64 partial dots of up to kDotBatch rows stay in registers
+// across the segments, and a butterfly over the wave ends each batch.  No
+// wave waits for another, so there is no barrier.  The two kinds of
+// workgroups are interleaved by token (a dot workgroup follows the copy
+// workgroups of the same four tokens), so grad_out is mostly read once.
+// ---------------------------------------------------------------------------
+template <int SEG>
+__device__ __forceinline__ void dot_token(const RowArgs &a, int64_t t, int lane)
+{
+    const int k = a.k;
+    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, true);
+    float mydw = 0.f;
+    const int nch = a.H >> 3;
+    constexpr int SPAN = SEG * kWave;
+    const int nseg = (nch + SPAN - 1) / SPAN;
+    uint64_t mrest = sl.prim_mask;
+    while (mrest) {
+        const Batch<kDotBatch> bt = take_batch<kDotBatch>(mrest, sl.row);
+        double part[kDotBatch];
+#pragma unroll
+        for (int b = 0; b < kDotBatch; ++b)
+            part[b] = 0.0;
+        for (int sg = 0; sg < nseg; ++sg) {
+            const int c0 = sg * SPAN;
+            u32x4 v[SEG];
+            load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
+            u32x4 f[kDotBatch][SEG];
+#pragma unroll
+            for (int b = 0; b < kDotBatch; ++b)
+                if (b < bt.n)
+                    load_seg<SEG, MOE_NT_DOT_F != 0>(f[b], a.F, bt.row[b], a.H, c0, nch, lane);
+#pragma unroll
+            for (int b = 0; b < kDotBatch; ++b) {
+                if (b < bt.n) {
+#pragma unroll
+                    for (int i = 0; i < SEG; ++i) {
+                        if (c0 + i * kWave + lane < nch) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const uint32_t gw = v[i][q], fw = f[b][i][q];
+                                part[b] = fma(static_cast<double>(bf16_lo(gw)),
+                                              static_cast<double>(bf16_lo(fw)), part[b]);
+                                part[b] = fma(static_cast<double>(bf16_hi(gw)),
+                                              static_cast<double>(bf16_hi(fw)), part[b]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kDotBatch; ++b) {
+            if (b < bt.n) {
+                double s = part[b];
+#pragma unroll
+                for (int o = kWave / 2; o >= 1; o >>= 1)
+                    s += __shfl_xor(s, o);
+                if (sl.valid && sl.first == bt.lane[b])
+                    mydw = static_cast<float>(s);
+            }
+        }
+    }
+    if (lane < k)
+        a.dw[t * k + lane] = sl.valid ? mydw : 0.f;
+}
+
+// Grid: [sentinel blocks][periods of (waves_per_token copy blocks, 1 dot
+// block), 4 tokens each][expert blocks].
+template <int SEG, int DSEG>
+__global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
+{
+    int64_t bid = blockIdx.x;
+    if (bid < a.nsent_blocks) {
+        fill_sentinel(a, bid);
+        return;
+    }
+    bid -= a.nsent_blocks;
+    const int64_t per = a.waves_per_token + 1;
+    const int64_t nmid = a.ndot_blocks * per;
+    if (bid < nmid) {
+        const int64_t period = bid / per;
+        const int pos = static_cast<int>(bid - period * per);
+        if (pos < a.waves_per_token) {
+            move_token<SEG>(a, period * a.waves_per_token + pos);
+        } else {
+            const int64_t t = period * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+            if (t < a.T)
+                dot_token<DSEG>(a, t, threadIdx.x & (kWave - 1));
+        }
+        return;
+    }
+    fill_expert(a, static_cast<int>(bid - nmid));
 }
 
 // ---------------------------------------------------------------------------
@@ -711,7 +740,10 @@ static int64_t sentinel_blocks(const RowArgs &a)
 void row_shape(RowArgs &a)
 {
     const int whole = chunks_per_lane(a.H);
-    const int cap = a.dw ? MOE_BWD_SEG : MOE_COPY_SEG;
+    const int cap = MOE_COPY_SEG;
+    a.dot_seg = whole < MOE_DOT_SEG ? whole : MOE_DOT_SEG;
+    // combine backward with dw: one dot workgroup per four tokens
+    a.ndot_blocks = a.dw ? (a.T + kRowWaves - 1) / kRowWaves : 0;
     a.seg = whole < cap ? whole : cap;
     const int nch = a.H >> 3;
     const int nseg = (nch + a.seg * kWave - 1) / (a.seg * kWave);
@@ -722,32 +754,39 @@ void row_shape(RowArgs &a)
     a.nsent_blocks = sentinel_blocks(a);
 }
 
-template <bool DOT>
-static void launch_move(int seg, dim3 g, const RowArgs &a, hipStream_t s)
-{
-    switch (seg) {
-    case 1: k_move_rows<1, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 2: k_move_rows<2, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    default: k_move_rows<4, DOT><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    }
-}
-
 hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
 {
-    const int64_t nb = a.ntok_blocks + a.nexp_blocks + a.nsent_blocks;
+    const int64_t nmid = a.dw ? a.ndot_blocks * (a.waves_per_token + 1) : a.ntok_blocks;
+    const int64_t nb = a.nsent_blocks + nmid + a.nexp_blocks;
     if (nb == 0)
         return hipSuccess;
     const dim3 g(static_cast<unsigned>(nb));
+    const dim3 blk(kRowThreads);
     if (a.rows_q) {
         switch (a.seg) {
-        case 1: k_dispatch_fp8<1><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-        case 2: k_dispatch_fp8<2><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-        default: k_dispatch_fp8<4><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+        case 1: k_dispatch_fp8<1><<<g, blk, 0, s>>>(a); break;
+        case 2: k_dispatch_fp8<2><<<g, blk, 0, s>>>(a); break;
+        default: k_dispatch_fp8<4><<<g, blk, 0, s>>>(a); break;
         }
-    } else if (a.dw)
-        launch_move<true>(a.seg, g, a, s);
-    else
-        launch_move<false>(a.seg, g, a, s);
+    } else if (a.dw) {
+        switch (a.seg * 8 + a.dot_seg) {
+        case 1 * 8 + 1: k_bwd_split<1, 1><<<g, blk, 0, s>>>(a); break;
+        case 1 * 8 + 2: k_bwd_split<1, 2><<<g, blk, 0, s>>>(a); break;
+        case 1 * 8 + 4: k_bwd_split<1, 4><<<g, blk, 0, s>>>(a); break;
+        case 2 * 8 + 1: k_bwd_split<2, 1><<<g, blk, 0, s>>>(a); break;
+        case 2 * 8 + 2: k_bwd_split<2, 2><<<g, blk, 0, s>>>(a); break;
+        case 2 * 8 + 4: k_bwd_split<2, 4><<<g, blk, 0, s>>>(a); break;
+        case 4 * 8 + 1: k_bwd_split<4, 1><<<g, blk, 0, s>>>(a); break;
+        case 4 * 8 + 2: k_bwd_split<4, 2><<<g, blk, 0, s>>>(a); break;
+        default: k_bwd_split<4, 4><<<g, blk, 0, s>>>(a); break;
+        }
+    } else {
+        switch (a.seg) {
+        case 1: k_move_rows<1><<<g, blk, 0, s>>>(a); break;
+        case 2: k_move_rows<2><<<g, blk, 0, s>>>(a); break;
+        default: k_move_rows<4><<<g, blk, 0, s>>>(a); break;
+        }
+    }
     return hipGetLastError();
 }
 
