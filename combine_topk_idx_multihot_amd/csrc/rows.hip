@@ -633,7 +633,8 @@ __global__ void __launch_bounds__(kRowThreads) k_dispatch_fp8(RowArgs a)
 // the weight gradients): one wave per (token, segment); the waves of a
 // workgroup read all segments of a token's rows at about the same time
 // ---------------------------------------------------------------------------
-template <int SEG, bool OUT_F32>
+// GW: the dispatch backward (also gathers the weight gradients of the slots).
+template <int SEG, bool OUT_F32, bool GW>
 __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -651,7 +652,7 @@ __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
     const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
     // dispatch backward: a slot's weight gradient is its row's (repeated ids
     // share the row, whose weight is the plain sum of theirs); 0 without a row
-    if (a.grad_w && c0 == 0 && lane < a.k)
+    if (GW && c0 == 0 && lane < a.k)
         a.grad_w[t * a.k + lane] = (sl.valid && a.grad_row_w) ? a.grad_row_w[sl.row] : 0.f;
     float acc[SEG][8];
 #pragma unroll
@@ -790,13 +791,13 @@ hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <bool F32>
+template <bool F32, bool GW>
 static void launch_comb(int seg, dim3 g, const CombineArgs &a, hipStream_t s)
 {
     switch (seg) {
-    case 1: k_combine<1, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 2: k_combine<2, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    default: k_combine<4, F32><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    case 1: k_combine<1, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    case 2: k_combine<2, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    default: k_combine<4, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
     }
 }
 
@@ -810,10 +811,11 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
     if (nb == 0)
         return hipSuccess;
     const dim3 g(static_cast<unsigned>(nb));
+    const bool gw = a.grad_w != nullptr;
     if (a.out_f32)
-        launch_comb<true>(seg, g, a, s);
+        gw ? launch_comb<true, true>(seg, g, a, s) : launch_comb<true, false>(seg, g, a, s);
     else
-        launch_comb<false>(seg, g, a, s);
+        gw ? launch_comb<false, true>(seg, g, a, s) : launch_comb<false, false>(seg, g, a, s);
     return hipGetLastError();
 }
 
