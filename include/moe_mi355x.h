@@ -108,7 +108,7 @@ typedef struct moe_handle {
 int64_t moe_capacity_min(const moe_desc *desc);
 
 /* Device bytes of handle.workspace for this description (0 if the description
- * is invalid): about ceil(T*k/1024) * (EL + 1) * 4 bytes. */
+ * is invalid): about ceil(T*k/512) * (EL + 1) * 4 bytes. */
 size_t moe_route_workspace_size(const moe_desc *desc);
 
 /*
