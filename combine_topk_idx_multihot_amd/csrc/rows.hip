@@ -63,6 +63,9 @@
 #ifndef MOE_FP8_HW
 #define MOE_FP8_HW 1
 #endif
+#ifndef MOE_BWD_XCD
+#define MOE_BWD_XCD 1
+#endif
 #ifndef MOE_DOT_SEG
 #define MOE_DOT_SEG 2
 #endif
@@ -459,6 +462,15 @@ __device__ __forceinline__ void dot_token(const RowArgs &a, int64_t t, int lane)
         a.dw[t * k + lane] = sl.valid ? mydw : 0.f;
 }
 
+// Workgroups of the middle part of the combine backward's grid: periods of
+// (waves_per_token copy workgroups, 1 dot workgroup), 4 tokens each; with the
+// XCD-aware order the periods are padded to a multiple of 8.
+__host__ __device__ __forceinline__ int64_t bwd_mid_blocks(const RowArgs &a)
+{
+    const int64_t np = MOE_BWD_XCD ? (a.ndot_blocks + 7) / 8 * 8 : a.ndot_blocks;
+    return np * (a.waves_per_token + 1);
+}
+
 // Grid: [sentinel blocks][periods of (waves_per_token copy blocks, 1 dot
 // block), 4 tokens each][expert blocks].
 template <int SEG, int DSEG>
@@ -471,10 +483,23 @@ __global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
     }
     bid -= a.nsent_blocks;
     const int64_t per = a.waves_per_token + 1;
-    const int64_t nmid = a.ndot_blocks * per;
+    const int64_t nmid = bwd_mid_blocks(a);
     if (bid < nmid) {
-        const int64_t period = bid / per;
-        const int pos = static_cast<int>(bid - period * per);
+        int64_t period, pos;
+        if (MOE_BWD_XCD) {
+            // Workgroup j is dispatched to XCD j % 8 (nsent_blocks is a
+            // multiple of 8): all workgroups of a period go to XCD period % 8,
+            // one after another, so the dot waves find grad_out in that
+            // XCD's L2 where the copy waves just read it.
+            const int64_t slot = bid >> 3;
+            period = (slot / per) * 8 + (bid & 7);
+            pos = slot % per;
+            if (period >= a.ndot_blocks)
+                return;
+        } else {
+            period = bid / per;
+            pos = bid - period * per;
+        }
         if (pos < a.waves_per_token) {
             move_token<SEG>(a, period * a.waves_per_token + pos);
         } else {
@@ -726,16 +751,18 @@ static int chunks_per_lane(int H)
 // handful for the (normally empty) [total, R).
 static int64_t sentinel_blocks(const RowArgs &a)
 {
+    // always a multiple of 8, so that the workgroups after them keep their
+    // index modulo the XCD count
     if (a.R <= 0)
-        return a.eager ? 1 : 0;
+        return a.eager ? 8 : 0;
     if (a.eager)
         return 8;
     // bytes per row: bf16 data, or E4M3 codes plus one fp32 scale per 128
     const int64_t row_bytes = a.rows_q ? a.H + (a.H >> 5) : 2 * static_cast<int64_t>(a.H);
     const int64_t bytes = a.R * row_bytes;
     const int64_t tasks = (bytes + 65535) / 65536;
-    const int64_t nb = (tasks + 4 * kRowWaves - 1) / (4 * kRowWaves);
-    return nb < 1 ? 1 : (nb > 4096 ? 4096 : nb);
+    const int64_t nb = ((tasks + 4 * kRowWaves - 1) / (4 * kRowWaves) + 7) / 8 * 8;
+    return nb > 4096 ? 4096 : nb;
 }
 
 void row_shape(RowArgs &a)
@@ -757,7 +784,7 @@ void row_shape(RowArgs &a)
 
 hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
 {
-    const int64_t nmid = a.dw ? a.ndot_blocks * (a.waves_per_token + 1) : a.ntok_blocks;
+    const int64_t nmid = a.dw ? bwd_mid_blocks(a) : a.ntok_blocks;
     const int64_t nb = a.nsent_blocks + nmid + a.nexp_blocks;
     if (nb == 0)
         return hipSuccess;
