@@ -194,3 +194,65 @@ def test_fp8_rows_dequantize_close_to_bf16_rows():
     err = (deq - ref).abs()
     bound = torch.maximum(ref.abs() * 2.0 ** -4, s.repeat_interleave(128, dim=1) * 2.0 ** -10)
     assert bool((err <= bound * (1 + 1e-5) + 1e-6 * ref.abs()).all())
+
+
+def test_fp8_sync_free_graph_replays_match_oracle():
+    """Sync-free route + FP8 dispatch captured once in a HIP graph, replayed on
+    three new inputs copied into the captured buffers (eager work between
+    replays); every replay is checked against the oracle row by row."""
+    T, E, k, lb, EL, P, H = 1000, 64, 6, 8, 24, 4, 768
+    C = oracle.capacity_min(T, k, EL, P) + 11
+    d = B.make_desc(T, k, E, lb, EL, P, B.MOE_SYNC_FREE, False, C)
+    dev = "cuda"
+    idx_t = torch.zeros((T, k), dtype=torch.int32, device=dev)
+    w_t = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    x_t = torch.zeros((T, H), dtype=torch.bfloat16, device=dev)
+    h = B.alloc_handle(d)
+    q = torch.empty((C, H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((C, H // 128), dtype=torch.float32, device=dev)
+    rw = torch.empty(C, dtype=torch.float32, device=dev)
+    rt = torch.empty(C, dtype=torch.int32, device=dev)
+    re = torch.empty(C, dtype=torch.int32, device=dev)
+
+    def case(seed):
+        rng = np.random.default_rng(seed)
+        idx = inputs.random_routing(T, E, k, rng, p_invalid=0.1, allow_dup=True)
+        return idx, rng.random((T, k), dtype=np.float32), inputs.bf16_normal((T, H), rng)
+
+    def load(c):
+        idx_t.copy_(torch.from_numpy(c[0].astype(np.int32)))
+        w_t.copy_(torch.from_numpy(c[1]))
+        x_t.copy_(to_dev_bf16(c[2]))
+
+    def step(stream):
+        B.moe_route_build(d, idx_t, h, stream=stream)
+        B.moe_dispatch_fp8(d, h, x_t, H, C, q, sc, w_t, rw, rt, re, stream=stream)
+
+    load(case(0))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(s)
+        torch.cuda.synchronize()
+        graph.capture_begin()
+        step(s)
+        graph.capture_end()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        say(f"[fp8 graph] replay seed={seed}")
+        c = case(seed)
+        load(c)
+        q.fill_(0x55)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.route(c[0], E, lb, EL, P, sync_free=True, C=C, w=c[1])
+        rq, rs = oracle.dispatch_fp8(c[2], ref.row_token)
+        np.testing.assert_array_equal(q.cpu().numpy(), rq)
+        np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+        np.testing.assert_array_equal(rt.cpu().numpy(), ref.row_token)
+        np.testing.assert_array_equal(re.cpu().numpy(), ref.row_expert)
+        np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+        _ = (x_t.float() * 2).sum().item()  # eager work between replays
