@@ -69,6 +69,15 @@
 #ifndef MOE_DOT_SEG
 #define MOE_DOT_SEG 2
 #endif
+#ifndef MOE_ZERO_MODE
+#define MOE_ZERO_MODE 0
+#endif
+#ifndef MOE_SENT_ONESHOT
+#define MOE_SENT_ONESHOT 2
+#endif
+#ifndef MOE_SENT_MAX
+#define MOE_SENT_MAX 4096
+#endif
 #ifndef MOE_COPY_BATCH
 #define MOE_COPY_BATCH 8
 #endif
@@ -189,8 +198,9 @@ __device__ __forceinline__ void load_seg(u32x4 (&v)[SEG], const uint16_t *base, 
     }
 }
 
-// Zero the 16-byte chunks [q0, q1) of `dst` in wave tasks of kZeroTask
-// contiguous chunks; wave `w` of `nw` takes tasks w, w + nw, ...
+// Zero the 16-byte chunks [q0, q1) of `dst`; wave `w` of `nw` takes part.
+#if MOE_ZERO_MODE == 0
+// Wave tasks of kZeroTask contiguous chunks: wave w takes tasks w, w + nw, ...
 __device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0, int64_t q1, int64_t w,
                                             int64_t nw, int lane)
 {
@@ -210,6 +220,26 @@ __device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0,
             put16<MOE_NT_ZERO != 0>(dst + i, z);
     }
 }
+#else
+// A window sliding through the range: on each pass the nw waves write
+// consecutive pieces of MOE_ZERO_MODE KiB (wave w the w-th), so the writes in
+// flight at any moment sit in one compact address range.
+__device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0, int64_t q1, int64_t w,
+                                            int64_t nw, int lane)
+{
+    constexpr int P = MOE_ZERO_MODE; // 1 KiB (64 chunks) per store instruction of the wave
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int64_t stride = nw * P * kWave;
+    for (int64_t b = q0 + w * P * kWave; b < q1; b += stride) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const int64_t i = b + j * kWave + lane;
+            if (i < q1)
+                put16<MOE_NT_ZERO != 0>(dst + i, z);
+        }
+    }
+}
+#endif
 
 // Zero the 4-byte words [w0, w1) of `base` (16-byte aligned): whole 16-byte
 // chunks as wave tasks, the unaligned head and tail (under 4 words each) by
@@ -352,9 +382,58 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
     zero_rows(a, pad0, hi, threadIdx.x / kWave, kRowWaves, tid & (kWave - 1));
 }
 
+// One-shot form of the sync-free tail fill (bf16 rows): wave gw of the
+// sentinel workgroups owns piece gw of the row array, MOE_SENT_ONESHOT KiB of
+// it, zeroes the part of it at or past row `total` and exits.  Workgroups
+// start in index order, so the pieces being written at any moment lie in one
+// window that slides through the tail.  The sentinel metadata of a row is
+// written by the wave whose piece holds the row's first chunk.
+__device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t sb)
+{
+    constexpr int64_t PC = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave; // chunks per piece
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gw = sb * kRowWaves + (threadIdx.x / kWave);
+    const int64_t nch = a.H >> 3;
+    const int64_t total = a.status[0];
+    const int64_t r0 = max<int64_t>(0, min<int64_t>(total, a.R));
+    const int64_t p0 = gw * PC;
+    const int64_t lo = max(p0, r0 * nch);
+    const int64_t hi = min(p0 + PC, a.R * nch);
+    if (lo >= hi)
+        return;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows);
+#pragma unroll
+    for (int j = 0; j < MOE_SENT_ONESHOT; ++j) {
+        const int64_t i = p0 + j * kWave + lane;
+        if (i >= lo && i < hi)
+            put16<MOE_NT_ZERO != 0>(dst + i, z);
+    }
+    const int64_t rf = max(r0, (p0 + nch - 1) / nch);
+    const int64_t rl = min(a.R, (p0 + PC + nch - 1) / nch);
+    for (int64_t r = rf + lane; r < rl; r += kWave) {
+        if (a.row_token)
+            a.row_token[r] = -1;
+        if (a.row_expert)
+            a.row_expert[r] = a.EL;
+        if (a.row_w)
+            a.row_w[r] = 0.f;
+    }
+}
+
+// Whether the sync-free tail is filled by one-shot waves (bf16 rows only).
+__host__ __device__ __forceinline__ bool sentinel_oneshot(const RowArgs &a)
+{
+    return MOE_SENT_ONESHOT > 0 && !a.eager && !a.rows_q;
+}
+
 // Rows [total, R): zero data, token -1, expert EL (the sentinel), weight 0.
 __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
 {
+    if (sentinel_oneshot(a)) {
+        fill_sentinel_oneshot(a, sb);
+        return;
+    }
     const int64_t total = a.status[0];
     const int64_t r0 = max<int64_t>(0, min<int64_t>(total, a.R));
     const int64_t r1 = a.R;
@@ -757,12 +836,19 @@ static int64_t sentinel_blocks(const RowArgs &a)
         return a.eager ? 8 : 0;
     if (a.eager)
         return 8;
+    if (sentinel_oneshot(a)) {
+        // one piece per wave over the whole row array (the host does not know
+        // where the tail starts)
+        const int64_t pieces = (a.R * (a.H >> 3) + MOE_SENT_ONESHOT * kWave - 1) /
+                               (MOE_SENT_ONESHOT * kWave);
+        return ((pieces + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
+    }
     // bytes per row: bf16 data, or E4M3 codes plus one fp32 scale per 128
     const int64_t row_bytes = a.rows_q ? a.H + (a.H >> 5) : 2 * static_cast<int64_t>(a.H);
     const int64_t bytes = a.R * row_bytes;
     const int64_t tasks = (bytes + 65535) / 65536;
     const int64_t nb = ((tasks + 4 * kRowWaves - 1) / (4 * kRowWaves) + 7) / 8 * 8;
-    return nb > 4096 ? 4096 : nb;
+    return nb > MOE_SENT_MAX ? MOE_SENT_MAX : nb;
 }
 
 void row_shape(RowArgs &a)
