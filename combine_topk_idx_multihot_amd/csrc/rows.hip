@@ -73,7 +73,10 @@
 #define MOE_ZERO_MODE 0
 #endif
 #ifndef MOE_SENT_ONESHOT
-#define MOE_SENT_ONESHOT 2
+#define MOE_SENT_ONESHOT 1
+#endif
+#ifndef MOE_SENT_SEPARATE
+#define MOE_SENT_SEPARATE 1
 #endif
 #ifndef MOE_SENT_MAX
 #define MOE_SENT_MAX 4096
@@ -382,49 +385,78 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
     zero_rows(a, pad0, hi, threadIdx.x / kWave, kRowWaves, tid & (kWave - 1));
 }
 
-// One-shot form of the sync-free tail fill (bf16 rows): wave gw of the
-// sentinel workgroups owns piece gw of the row array, MOE_SENT_ONESHOT KiB of
-// it, zeroes the part of it at or past row `total` and exits.  Workgroups
-// start in index order, so the pieces being written at any moment lie in one
-// window that slides through the tail.  The sentinel metadata of a row is
-// written by the wave whose piece holds the row's first chunk.
+// One-shot form of the sync-free tail fill: wave gw of the sentinel grid owns
+// piece gw, MOE_SENT_ONESHOT KiB of the row array (bf16 rows, or E4M3 rows
+// followed by their scale array), zeroes the part of it at or past row
+// `total` and exits.  Workgroups start in index order, so the pieces being
+// written at any moment lie in one window that slides through the tail.  The
+// sentinel metadata of a row is written by the wave whose piece holds the
+// row's first chunk.
 __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t sb)
 {
-    constexpr int64_t PC = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave; // chunks per piece
+    constexpr int64_t PC = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave; // 16-byte chunks per piece
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = sb * kRowWaves + (threadIdx.x / kWave);
-    const int64_t nch = a.H >> 3;
     const int64_t total = a.status[0];
     const int64_t r0 = max<int64_t>(0, min<int64_t>(total, a.R));
-    const int64_t p0 = gw * PC;
-    const int64_t lo = max(p0, r0 * nch);
-    const int64_t hi = min(p0 + PC, a.R * nch);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int64_t nch = a.rows_q ? (a.H >> 4) : (a.H >> 3); // chunks per row
+    const int64_t nrow_pieces = (a.R * nch + PC - 1) / PC;
+    if (gw < nrow_pieces) {
+        const int64_t p0 = gw * PC;
+        const int64_t lo = max(p0, r0 * nch);
+        const int64_t hi = min(p0 + PC, a.R * nch);
+        if (lo >= hi)
+            return;
+        u32x4 *__restrict__ dst = a.rows_q ? reinterpret_cast<u32x4 *>(a.rows_q)
+                                           : reinterpret_cast<u32x4 *>(a.rows);
+#pragma unroll
+        for (int j = 0; j < MOE_SENT_ONESHOT; ++j) {
+            const int64_t i = p0 + j * kWave + lane;
+            if (i >= lo && i < hi)
+                put16<MOE_NT_ZERO != 0>(dst + i, z);
+        }
+        const int64_t rf = max(r0, (p0 + nch - 1) / nch);
+        const int64_t rl = min(a.R, (p0 + PC + nch - 1) / nch);
+        for (int64_t r = rf + lane; r < rl; r += kWave) {
+            if (a.row_token)
+                a.row_token[r] = -1;
+            if (a.row_expert)
+                a.row_expert[r] = a.EL;
+            if (a.row_w)
+                a.row_w[r] = 0.f;
+        }
+        return;
+    }
+    if (!a.rows_q)
+        return;
+    // E4M3 scales: words [r0 * nb, R * nb), pieces of PC * 4 words; a chunk
+    // that straddles the start of the tail is written word by word
+    const int64_t nb = a.H >> 7;
+    const int64_t w0 = (gw - nrow_pieces) * PC * 4;
+    const int64_t lo = max(w0, r0 * nb);
+    const int64_t hi = min(w0 + PC * 4, a.R * nb);
     if (lo >= hi)
         return;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows);
+    uint32_t *__restrict__ base = reinterpret_cast<uint32_t *>(a.row_scale);
 #pragma unroll
     for (int j = 0; j < MOE_SENT_ONESHOT; ++j) {
-        const int64_t i = p0 + j * kWave + lane;
-        if (i >= lo && i < hi)
-            put16<MOE_NT_ZERO != 0>(dst + i, z);
-    }
-    const int64_t rf = max(r0, (p0 + nch - 1) / nch);
-    const int64_t rl = min(a.R, (p0 + PC + nch - 1) / nch);
-    for (int64_t r = rf + lane; r < rl; r += kWave) {
-        if (a.row_token)
-            a.row_token[r] = -1;
-        if (a.row_expert)
-            a.row_expert[r] = a.EL;
-        if (a.row_w)
-            a.row_w[r] = 0.f;
+        const int64_t w = w0 + (j * kWave + lane) * 4;
+        if (w >= lo && w + 4 <= hi) {
+            put16<MOE_NT_ZERO != 0>(reinterpret_cast<u32x4 *>(base + w), z);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (w + q >= lo && w + q < hi)
+                    base[w + q] = 0u;
+        }
     }
 }
 
-// Whether the sync-free tail is filled by one-shot waves (bf16 rows only).
+// Whether the sync-free tail is filled by one-shot waves.
 __host__ __device__ __forceinline__ bool sentinel_oneshot(const RowArgs &a)
 {
-    return MOE_SENT_ONESHOT > 0 && !a.eager && !a.rows_q;
+    return MOE_SENT_ONESHOT > 0 && !a.eager;
 }
 
 // Rows [total, R): zero data, token -1, expert EL (the sentinel), weight 0.
@@ -838,9 +870,12 @@ static int64_t sentinel_blocks(const RowArgs &a)
         return 8;
     if (sentinel_oneshot(a)) {
         // one piece per wave over the whole row array (the host does not know
-        // where the tail starts)
-        const int64_t pieces = (a.R * (a.H >> 3) + MOE_SENT_ONESHOT * kWave - 1) /
-                               (MOE_SENT_ONESHOT * kWave);
+        // where the tail starts), and over the scale array of E4M3 rows
+        const int64_t pc = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave;
+        const int64_t nch = a.rows_q ? (a.H >> 4) : (a.H >> 3);
+        int64_t pieces = (a.R * nch + pc - 1) / pc;
+        if (a.rows_q)
+            pieces += (a.R * (a.H >> 7) + pc * 4 - 1) / (pc * 4);
         return ((pieces + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
     }
     // bytes per row: bf16 data, or E4M3 codes plus one fp32 scale per 128
@@ -868,8 +903,20 @@ void row_shape(RowArgs &a)
     a.nsent_blocks = sentinel_blocks(a);
 }
 
-hipError_t launch_move_rows(const RowArgs &a, hipStream_t s)
+// The one-shot tail fill as a launch of its own (MOE_SENT_SEPARATE).
+__global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
 {
+    fill_sentinel_oneshot(a, blockIdx.x);
+}
+
+hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
+{
+    RowArgs a = a0;
+    if (MOE_SENT_SEPARATE && sentinel_oneshot(a0) && a0.nsent_blocks > 0) {
+        // the tail first, on its own, then the rows
+        k_sentinel_oneshot<<<dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s>>>(a0);
+        a.nsent_blocks = 0;
+    }
     const int64_t nmid = a.dw ? bwd_mid_blocks(a) : a.ntok_blocks;
     const int64_t nb = a.nsent_blocks + nmid + a.nexp_blocks;
     if (nb == 0)
