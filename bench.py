@@ -24,7 +24,10 @@ Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
 (event-timed) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
 host on a bounded sample of the same workload.  `next` times, outside the
-step, the FP8 dispatch and the dispatch backward on the same routings.
+step, the FP8 dispatch and the dispatch backward on the same routings.  The
+metric is quoted at 4096 and at 16384 tokens, so `also` repeats the step
+(value and roofline) on the 16384-token, H = 4096 layers after the main one
+(`--companions`).
 """
 from __future__ import annotations
 
@@ -82,6 +85,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall budget of the oracle CPU-baseline leg (0 = skip)")
+    ap.add_argument("--companions", default="h4096_rank_share,backward_h4096",
+                    help="workloads also timed (value and roofline only) after the main one; "
+                         "'' for none")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the FP8 dispatch and the dispatch backward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -102,10 +108,33 @@ def main():
     from combine_topk_idx_multihot_amd import binding as B
     from combine_topk_idx_multihot_amd import inputs
 
-    wl = inputs.WORKLOADS[args.workload]
+    B.moe_device_check(0)
+    result, sets, wl = measure(args.workload, args, not args.no_next, torch, B, inputs)
+
+    # ---- CPU baseline: the oracle on the host, bounded sample ---------------
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, sets[0], args.cpu_seconds, torch)
+    del sets
+
+    # ---- the metric's 16384-token layers, alongside the 4096-token one -------
+    comp = [c for c in args.companions.split(",") if c and c != args.workload]
+    if comp:
+        result["also"] = {}
+        for name in comp:
+            torch.cuda.empty_cache()
+            r, s_, _ = measure(name, args, False, torch, B, inputs)
+            del s_
+            result["also"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "config",
+                                                      "us_per_layer", "roofline")}
+    print(json.dumps(result), flush=True)
+
+
+def measure(name, args, with_next, torch, B, inputs):
+    """Warm up, take the per-kernel breakdown, then time K steps of workload
+    `name`.  Returns (result fields, buffer sets, workload)."""
+    wl = inputs.WORKLOADS[name]
     seed0 = args.seed if args.seed is not None else 1000 + list(inputs.WORKLOADS).index(wl.name) + 1
     dev = torch.device("cuda:0")
-    B.moe_device_check(0)
     stream = torch.cuda.current_stream()
     EL = wl.num_local
     mode = B.MOE_SYNC_FREE if wl.sync_free else B.MOE_EAGER
@@ -245,13 +274,9 @@ def main():
     }
 
     result["roofline"]["traffic"] = measured_traffic(wl.name, dominant)
-    if not args.no_next:
+    if with_next:
         result["next"] = time_next(wl, d, sets, facts, args.steps, stream, torch, B, kern)
-
-    # ---- CPU baseline: the oracle on the host, bounded sample ---------------
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(wl, sets[0], args.cpu_seconds, torch)
-    print(json.dumps(result), flush=True)
+    return result, sets, wl
 
 
 def time_next(wl, d, sets, facts, steps, stream, torch, B, kern):
