@@ -71,7 +71,7 @@ int check_desc(const moe_desc *d)
         return fail(MOE_ERR_ARG, "idx_is_i64 must be 0 or 1 (got %d)", d->idx_is_i64);
     if (d->reserved != 0)
         return fail(MOE_ERR_ARG, "reserved must be 0");
-    if (d->T * d->k > kI32Max || cap_min(d) > kI32Max)
+    if (d->T > kI32Max || d->T * d->k > kI32Max || cap_min(d) > kI32Max)
         return fail(MOE_ERR_ARG, "T*k and the worst-case row count must fit in int32");
     if (d->mode == MOE_SYNC_FREE) {
         if (d->capacity < cap_min(d))

@@ -7,6 +7,10 @@
 
 namespace moe {
 
+// Largest grid (x) dimension a launch may use; launches that would need more
+// return hipErrorInvalidConfiguration instead of truncating the count.
+constexpr int64_t kMaxGrid = 2147483647;
+
 constexpr int kWave = 64;
 constexpr int kMaxK = 64;         // slots per token handled lane-parallel by one wave
 constexpr int kMaxLocal = 1024;   // local experts (LDS bitmap bound)

@@ -912,6 +912,8 @@ __global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
 hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
 {
     RowArgs a = a0;
+    if (a0.nsent_blocks + a0.ntok_blocks + a0.nexp_blocks + bwd_mid_blocks(a0) > kMaxGrid)
+        return hipErrorInvalidConfiguration;
     if (MOE_SENT_SEPARATE && sentinel_oneshot(a0) && a0.nsent_blocks > 0) {
         // the tail first, on its own, then the rows
         k_sentinel_oneshot<<<dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s>>>(a0);
@@ -970,6 +972,8 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
     const int64_t nb = (a.T * nseg + kRowWaves - 1) / kRowWaves;
     if (nb == 0)
         return hipSuccess;
+    if (nb > kMaxGrid)
+        return hipErrorInvalidConfiguration;
     const dim3 g(static_cast<unsigned>(nb));
     const bool gw = a.grad_w != nullptr;
     if (a.out_f32)

@@ -256,3 +256,34 @@ def test_fp8_sync_free_graph_replays_match_oracle():
         np.testing.assert_array_equal(re.cpu().numpy(), ref.row_expert)
         np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
         _ = (x_t.float() * 2).sum().item()  # eager work between replays
+
+
+def test_fp8_eager_rows_mismatch_flag():
+    """Eager mode with R above the routed total: rows past the total become
+    sentinel rows (zero codes, zero scales, expert EL) and flag bit 2 is set."""
+    rng = np.random.default_rng(4)
+    T, E, k, H = 64, 8, 2, 768
+    idx = inputs.random_routing(T, E, k, rng)
+    d = B.make_desc(T, k, E, pad_multiple=1)
+    h, _ = B.route(d, torch.from_numpy(idx.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    total = h.total
+    x = to_dev_bf16(inputs.bf16_normal((T, H), rng))
+    R = total + 9
+    q = torch.full((R, H), 0x55, dtype=torch.uint8, device="cuda")
+    sc = torch.full((R, H // 128), 7.0, dtype=torch.float32, device="cuda")
+    re = torch.empty(R, dtype=torch.int32, device="cuda")
+    say("[fp8 eager mismatch]")
+    B.moe_dispatch_fp8(d, h, x, H, R, q, sc, row_expert=re)
+    torch.cuda.synchronize()
+    assert int(h.status[1]) & B.MOE_FLAG_ROWS_MISMATCH
+    assert not q[total:].any() and not sc[total:].any()
+    assert (re[total:].cpu().numpy() == E).all()
+    ref = oracle.route(idx, E)
+    rq, rs = oracle.dispatch_fp8(to_np(x), ref.row_token)
+    np.testing.assert_array_equal(q[:total].cpu().numpy(), rq)
+    np.testing.assert_array_equal(sc[:total].cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def to_np(t):
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
