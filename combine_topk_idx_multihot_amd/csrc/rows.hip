@@ -28,10 +28,14 @@
 //     walks the row and keeps its partial dots in registers, a butterfly
 //     over the wave ends each dot, so dw is the same on every run and no
 //     wave waits for another.
-//   * pad rows (one workgroup per expert) and the sentinel tail [total, R)
-//     are zeroed by extra workgroups of the same launch.  The tail is one
-//     contiguous range, cut into 64 KiB wave tasks: a contiguous stream per
-//     wave writes HBM markedly faster than a grid-stride pattern on MI355X.
+//   * pad rows are zeroed by extra workgroups of the rows' launch (one per
+//     expert).  The sync-free tail [total, R) -- most of the bytes when the
+//     worst case is far from the routed total -- is a launch of its own just
+//     before, of one-shot waves that each zero one 1 KiB piece in address
+//     order: the writes in flight then form one window sliding through the
+//     tail, which MI355X's HBM takes markedly faster than the same writes
+//     spread over the range.  In eager mode the tail is normally empty; a few
+//     workgroups of the rows' launch cover it in 64 KiB wave tasks.
 //   * combine adds the token's rows in fp32 in ascending slot order (the
 //     accumulator starts from the first row) and writes bf16 (nearest-even)
 //     or fp32; one wave per (token, segment).
@@ -63,23 +67,11 @@
 #ifndef MOE_FP8_HW
 #define MOE_FP8_HW 1
 #endif
-#ifndef MOE_BWD_XCD
-#define MOE_BWD_XCD 1
-#endif
 #ifndef MOE_DOT_SEG
 #define MOE_DOT_SEG 2
 #endif
-#ifndef MOE_ZERO_MODE
-#define MOE_ZERO_MODE 0
-#endif
-#ifndef MOE_SENT_ONESHOT
-#define MOE_SENT_ONESHOT 1
-#endif
-#ifndef MOE_SENT_SEPARATE
-#define MOE_SENT_SEPARATE 1
-#endif
-#ifndef MOE_SENT_MAX
-#define MOE_SENT_MAX 4096
+#ifndef MOE_TAIL_PIECE_KIB
+#define MOE_TAIL_PIECE_KIB 1
 #endif
 #ifndef MOE_COPY_BATCH
 #define MOE_COPY_BATCH 8
@@ -201,9 +193,8 @@ __device__ __forceinline__ void load_seg(u32x4 (&v)[SEG], const uint16_t *base, 
     }
 }
 
-// Zero the 16-byte chunks [q0, q1) of `dst`; wave `w` of `nw` takes part.
-#if MOE_ZERO_MODE == 0
-// Wave tasks of kZeroTask contiguous chunks: wave w takes tasks w, w + nw, ...
+// Zero the 16-byte chunks [q0, q1) of `dst` in wave tasks of kZeroTask
+// contiguous chunks; wave `w` of `nw` takes tasks w, w + nw, ...
 __device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0, int64_t q1, int64_t w,
                                             int64_t nw, int lane)
 {
@@ -223,26 +214,6 @@ __device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0,
             put16<MOE_NT_ZERO != 0>(dst + i, z);
     }
 }
-#else
-// A window sliding through the range: on each pass the nw waves write
-// consecutive pieces of MOE_ZERO_MODE KiB (wave w the w-th), so the writes in
-// flight at any moment sit in one compact address range.
-__device__ __forceinline__ void zero_chunks(u32x4 *__restrict__ dst, int64_t q0, int64_t q1, int64_t w,
-                                            int64_t nw, int lane)
-{
-    constexpr int P = MOE_ZERO_MODE; // 1 KiB (64 chunks) per store instruction of the wave
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const int64_t stride = nw * P * kWave;
-    for (int64_t b = q0 + w * P * kWave; b < q1; b += stride) {
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const int64_t i = b + j * kWave + lane;
-            if (i < q1)
-                put16<MOE_NT_ZERO != 0>(dst + i, z);
-        }
-    }
-}
-#endif
 
 // Zero the 4-byte words [w0, w1) of `base` (16-byte aligned): whole 16-byte
 // chunks as wave tasks, the unaligned head and tail (under 4 words each) by
@@ -386,7 +357,7 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
 }
 
 // One-shot form of the sync-free tail fill: wave gw of the sentinel grid owns
-// piece gw, MOE_SENT_ONESHOT KiB of the row array (bf16 rows, or E4M3 rows
+// piece gw, MOE_TAIL_PIECE_KIB KiB of the row array (bf16 rows, or E4M3 rows
 // followed by their scale array), zeroes the part of it at or past row
 // `total` and exits.  Workgroups start in index order, so the pieces being
 // written at any moment lie in one window that slides through the tail.  The
@@ -394,7 +365,7 @@ __device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
 // row's first chunk.
 __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t sb)
 {
-    constexpr int64_t PC = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave; // 16-byte chunks per piece
+    constexpr int64_t PC = static_cast<int64_t>(MOE_TAIL_PIECE_KIB) * kWave; // 16-byte chunks per piece
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t gw = sb * kRowWaves + (threadIdx.x / kWave);
     const int64_t total = a.status[0];
@@ -411,7 +382,7 @@ __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t 
         u32x4 *__restrict__ dst = a.rows_q ? reinterpret_cast<u32x4 *>(a.rows_q)
                                            : reinterpret_cast<u32x4 *>(a.rows);
 #pragma unroll
-        for (int j = 0; j < MOE_SENT_ONESHOT; ++j) {
+        for (int j = 0; j < MOE_TAIL_PIECE_KIB; ++j) {
             const int64_t i = p0 + j * kWave + lane;
             if (i >= lo && i < hi)
                 put16<MOE_NT_ZERO != 0>(dst + i, z);
@@ -440,7 +411,7 @@ __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t 
         return;
     uint32_t *__restrict__ base = reinterpret_cast<uint32_t *>(a.row_scale);
 #pragma unroll
-    for (int j = 0; j < MOE_SENT_ONESHOT; ++j) {
+    for (int j = 0; j < MOE_TAIL_PIECE_KIB; ++j) {
         const int64_t w = w0 + (j * kWave + lane) * 4;
         if (w >= lo && w + 4 <= hi) {
             put16<MOE_NT_ZERO != 0>(reinterpret_cast<u32x4 *>(base + w), z);
@@ -453,19 +424,11 @@ __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t 
     }
 }
 
-// Whether the sync-free tail is filled by one-shot waves.
-__host__ __device__ __forceinline__ bool sentinel_oneshot(const RowArgs &a)
-{
-    return MOE_SENT_ONESHOT > 0 && !a.eager;
-}
-
-// Rows [total, R): zero data, token -1, expert EL (the sentinel), weight 0.
+// Rows [total, R) in eager mode (normally none: R is the total read back;
+// a different R sets flag bit 2): zero data, token -1, expert EL (the
+// sentinel), weight 0, by a few workgroups of the rows' launch.
 __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
 {
-    if (sentinel_oneshot(a)) {
-        fill_sentinel_oneshot(a, sb);
-        return;
-    }
     const int64_t total = a.status[0];
     const int64_t r0 = max<int64_t>(0, min<int64_t>(total, a.R));
     const int64_t r1 = a.R;
@@ -578,7 +541,7 @@ __device__ __forceinline__ void dot_token(const RowArgs &a, int64_t t, int lane)
 // XCD-aware order the periods are padded to a multiple of 8.
 __host__ __device__ __forceinline__ int64_t bwd_mid_blocks(const RowArgs &a)
 {
-    const int64_t np = MOE_BWD_XCD ? (a.ndot_blocks + 7) / 8 * 8 : a.ndot_blocks;
+    const int64_t np = (a.ndot_blocks + 7) / 8 * 8;
     return np * (a.waves_per_token + 1);
 }
 
@@ -596,21 +559,15 @@ __global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
     const int64_t per = a.waves_per_token + 1;
     const int64_t nmid = bwd_mid_blocks(a);
     if (bid < nmid) {
-        int64_t period, pos;
-        if (MOE_BWD_XCD) {
-            // Workgroup j is dispatched to XCD j % 8 (nsent_blocks is a
-            // multiple of 8): all workgroups of a period go to XCD period % 8,
-            // one after another, so the dot waves find grad_out in that
-            // XCD's L2 where the copy waves just read it.
-            const int64_t slot = bid >> 3;
-            period = (slot / per) * 8 + (bid & 7);
-            pos = slot % per;
-            if (period >= a.ndot_blocks)
-                return;
-        } else {
-            period = bid / per;
-            pos = bid - period * per;
-        }
+        // Workgroup j is dispatched to XCD j % 8 (nsent_blocks is a multiple
+        // of 8): all workgroups of a period go to XCD period % 8, one after
+        // another, so the dot waves find grad_out in that XCD's L2 where the
+        // copy waves just read it.
+        const int64_t slot = bid >> 3;
+        const int64_t period = (slot / per) * 8 + (bid & 7);
+        const int64_t pos = slot % per;
+        if (period >= a.ndot_blocks)
+            return;
         if (pos < a.waves_per_token) {
             move_token<SEG>(a, period * a.waves_per_token + pos);
         } else {
@@ -864,26 +821,17 @@ static int64_t sentinel_blocks(const RowArgs &a)
 {
     // always a multiple of 8, so that the workgroups after them keep their
     // index modulo the XCD count
-    if (a.R <= 0)
-        return a.eager ? 8 : 0;
     if (a.eager)
         return 8;
-    if (sentinel_oneshot(a)) {
-        // one piece per wave over the whole row array (the host does not know
-        // where the tail starts), and over the scale array of E4M3 rows
-        const int64_t pc = static_cast<int64_t>(MOE_SENT_ONESHOT) * kWave;
-        const int64_t nch = a.rows_q ? (a.H >> 4) : (a.H >> 3);
-        int64_t pieces = (a.R * nch + pc - 1) / pc;
-        if (a.rows_q)
-            pieces += (a.R * (a.H >> 7) + pc * 4 - 1) / (pc * 4);
-        return ((pieces + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
-    }
-    // bytes per row: bf16 data, or E4M3 codes plus one fp32 scale per 128
-    const int64_t row_bytes = a.rows_q ? a.H + (a.H >> 5) : 2 * static_cast<int64_t>(a.H);
-    const int64_t bytes = a.R * row_bytes;
-    const int64_t tasks = (bytes + 65535) / 65536;
-    const int64_t nb = ((tasks + 4 * kRowWaves - 1) / (4 * kRowWaves) + 7) / 8 * 8;
-    return nb > MOE_SENT_MAX ? MOE_SENT_MAX : nb;
+    // sync-free: the tail's own launch, one piece per wave over the whole row
+    // array (the host does not know where the tail starts), and over the
+    // scale array of E4M3 rows
+    const int64_t pc = static_cast<int64_t>(MOE_TAIL_PIECE_KIB) * kWave;
+    const int64_t nch = a.rows_q ? (a.H >> 4) : (a.H >> 3);
+    int64_t pieces = (a.R * nch + pc - 1) / pc;
+    if (a.rows_q)
+        pieces += (a.R * (a.H >> 7) + pc * 4 - 1) / (pc * 4);
+    return ((pieces + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
 }
 
 void row_shape(RowArgs &a)
@@ -903,7 +851,7 @@ void row_shape(RowArgs &a)
     a.nsent_blocks = sentinel_blocks(a);
 }
 
-// The one-shot tail fill as a launch of its own (MOE_SENT_SEPARATE).
+// The sync-free tail fill, a launch of its own.
 __global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
 {
     fill_sentinel_oneshot(a, blockIdx.x);
@@ -914,8 +862,8 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
     RowArgs a = a0;
     if (a0.nsent_blocks + a0.ntok_blocks + a0.nexp_blocks + bwd_mid_blocks(a0) > kMaxGrid)
         return hipErrorInvalidConfiguration;
-    if (MOE_SENT_SEPARATE && sentinel_oneshot(a0) && a0.nsent_blocks > 0) {
-        // the tail first, on its own, then the rows
+    if (!a0.eager && a0.nsent_blocks > 0) {
+        // sync-free: the tail first, on its own, then the rows
         k_sentinel_oneshot<<<dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s>>>(a0);
         a.nsent_blocks = 0;
     }
