@@ -195,6 +195,7 @@ int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16
     a.R = R;
     a.k = desc->k;
     a.EL = desc->num_local;
+    a.E_total = desc->E;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
     moe::row_shape(a);
@@ -419,6 +420,7 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     a.R = R;
     a.k = desc->k;
     a.EL = desc->num_local;
+    a.E_total = desc->E;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
     moe::row_shape(a);

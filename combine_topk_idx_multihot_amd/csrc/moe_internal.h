@@ -65,12 +65,14 @@ struct RowArgs {
     int32_t *status;
     int64_t T, R;
     int32_t k, EL, H;
+    int32_t E_total;           // all experts (E), for launch heuristics
     int32_t eager;
     int32_t seg;               // 16-byte chunks per lane per segment
     int32_t waves_per_token;   // 1, 2 or 4: a token's segments are dealt over these waves
-    int32_t dot_seg;           // combine backward, split form: chunks per lane per dot segment
+    int32_t dot_seg;           // combine backward: chunks per lane per dot segment
+    int32_t dot_wpt;           // combine backward: waves sharing one token's dots (1, 2 or 4)
     int64_t ntok_blocks, nexp_blocks, nsent_blocks;
-    int64_t ndot_blocks;       // split form: dot workgroups (4 tokens each), 0 otherwise
+    int64_t ndot_blocks;       // combine backward with dw: periods of 4 tokens, 0 otherwise
 };
 
 // Row movement: dispatch (x -> rows, or with rows_q set x -> E4M3 rows and

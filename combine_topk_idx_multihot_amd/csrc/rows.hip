@@ -67,8 +67,14 @@
 #ifndef MOE_FP8_HW
 #define MOE_FP8_HW 1
 #endif
+#ifndef MOE_DOT_MAX_WPT
+#define MOE_DOT_MAX_WPT 4
+#endif
 #ifndef MOE_DOT_SEG
-#define MOE_DOT_SEG 2
+#define MOE_DOT_SEG 1
+#endif
+#ifndef MOE_DOT_SEG_SPARSE
+#define MOE_DOT_SEG_SPARSE 2
 #endif
 #ifndef MOE_TAIL_PIECE_KIB
 #define MOE_TAIL_PIECE_KIB 1
@@ -468,52 +474,67 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 
 // ---------------------------------------------------------------------------
 // combine backward, split form: the grad rows are a plain dispatch of
-// grad_out (move_token without dots), and dw comes from separate waves that
-// each own one token: the token's row is walked in segments of SEG chunks
-// per lane, the fp64 partial dots of up to kDotBatch rows stay in registers
-// across the segments, and a butterfly over the wave ends each batch.  No
-// wave waits for another, so there is no barrier.  The two kinds of
-// workgroups are interleaved by token (a dot workgroup follows the copy
-// workgroups of the same four tokens), so grad_out is mostly read once.
+// grad_out (move_token), and dw comes from dot workgroups of their own.  In a
+// dot workgroup a token's row is dealt over dot_wpt waves (1, 2 or 4), each
+// walking its segments of SEG chunks per lane with the fp64 partial dots of
+// up to kDotBatch rows in registers; a butterfly over each wave, then the
+// token's first wave adding its waves' sums in wave order through LDS, end
+// each batch.  So dw is the same on every run.  The dot workgroups hold only
+// dot waves, all running the same number of batch rounds, so their barriers
+// never wait on copying work.  Copy and dot workgroups are interleaved by
+// token: every four tokens get waves_per_token copy workgroups, then dot_wpt
+// dot workgroups.
 // ---------------------------------------------------------------------------
 template <int SEG>
-__device__ __forceinline__ void dot_token(const RowArgs &a, int64_t t, int lane)
+__device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
 {
+    __shared__ double red[kRowWaves][kDotBatch];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wpt = a.dot_wpt;
+    const int tl = wave / wpt;
+    const int wt = wave - tl * wpt;
+    const int64_t t = db * (kRowWaves / wpt) + tl;
+    const bool active = t < a.T;
     const int k = a.k;
-    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, true);
+    const Slots sl = load_slots(a.row_of_slot, t, k, a.R, lane, active);
     float mydw = 0.f;
     const int nch = a.H >> 3;
     constexpr int SPAN = SEG * kWave;
     const int nseg = (nch + SPAN - 1) / SPAN;
+    // the same number of rounds in every wave of the workgroup (barriers)
+    const int rounds = (k + kDotBatch - 1) / kDotBatch;
     uint64_t mrest = sl.prim_mask;
-    while (mrest) {
+    for (int rd = 0; rd < rounds; ++rd) {
         const Batch<kDotBatch> bt = take_batch<kDotBatch>(mrest, sl.row);
         double part[kDotBatch];
 #pragma unroll
         for (int b = 0; b < kDotBatch; ++b)
             part[b] = 0.0;
-        for (int sg = 0; sg < nseg; ++sg) {
-            const int c0 = sg * SPAN;
-            u32x4 v[SEG];
-            load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
-            u32x4 f[kDotBatch][SEG];
+        if (bt.n > 0) {
+            for (int sg = wt; sg < nseg; sg += wpt) {
+                const int c0 = sg * SPAN;
+                u32x4 v[SEG];
+                load_seg<SEG>(v, a.src, t, a.H, c0, nch, lane);
+                u32x4 f[kDotBatch][SEG];
 #pragma unroll
-            for (int b = 0; b < kDotBatch; ++b)
-                if (b < bt.n)
-                    load_seg<SEG, MOE_NT_DOT_F != 0>(f[b], a.F, bt.row[b], a.H, c0, nch, lane);
+                for (int b = 0; b < kDotBatch; ++b)
+                    if (b < bt.n)
+                        load_seg<SEG, MOE_NT_DOT_F != 0>(f[b], a.F, bt.row[b], a.H, c0, nch, lane);
 #pragma unroll
-            for (int b = 0; b < kDotBatch; ++b) {
-                if (b < bt.n) {
+                for (int b = 0; b < kDotBatch; ++b) {
+                    if (b < bt.n) {
 #pragma unroll
-                    for (int i = 0; i < SEG; ++i) {
-                        if (c0 + i * kWave + lane < nch) {
+                        for (int i = 0; i < SEG; ++i) {
+                            if (c0 + i * kWave + lane < nch) {
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const uint32_t gw = v[i][q], fw = f[b][i][q];
-                                part[b] = fma(static_cast<double>(bf16_lo(gw)),
-                                              static_cast<double>(bf16_lo(fw)), part[b]);
-                                part[b] = fma(static_cast<double>(bf16_hi(gw)),
-                                              static_cast<double>(bf16_hi(fw)), part[b]);
+                                for (int q = 0; q < 4; ++q) {
+                                    const uint32_t gw = v[i][q], fw = f[b][i][q];
+                                    part[b] = fma(static_cast<double>(bf16_lo(gw)),
+                                                  static_cast<double>(bf16_lo(fw)), part[b]);
+                                    part[b] = fma(static_cast<double>(bf16_hi(gw)),
+                                                  static_cast<double>(bf16_hi(fw)), part[b]);
+                                }
                             }
                         }
                     }
@@ -523,30 +544,49 @@ __device__ __forceinline__ void dot_token(const RowArgs &a, int64_t t, int lane)
 #pragma unroll
         for (int b = 0; b < kDotBatch; ++b) {
             if (b < bt.n) {
-                double s = part[b];
+                double sum = part[b];
 #pragma unroll
                 for (int o = kWave / 2; o >= 1; o >>= 1)
-                    s += __shfl_xor(s, o);
-                if (sl.valid && sl.first == bt.lane[b])
-                    mydw = static_cast<float>(s);
+                    sum += __shfl_xor(sum, o);
+                if (lane == 0)
+                    red[wave][b] = sum;
             }
         }
+        __syncthreads();
+        if (wt == 0) {
+#pragma unroll
+            for (int b = 0; b < kDotBatch; ++b) {
+                if (b < bt.n) {
+                    double sum = red[wave][b];
+                    for (int w = 1; w < wpt; ++w)
+                        sum += red[wave + w][b];
+                    if (sl.valid && sl.first == bt.lane[b])
+                        mydw = static_cast<float>(sum);
+                }
+            }
+        }
+        __syncthreads();
     }
-    if (lane < k)
+    if (active && wt == 0 && lane < k)
         a.dw[t * k + lane] = sl.valid ? mydw : 0.f;
 }
 
-// Workgroups of the middle part of the combine backward's grid: periods of
-// (waves_per_token copy workgroups, 1 dot workgroup), 4 tokens each; with the
-// XCD-aware order the periods are padded to a multiple of 8.
+// Workgroups per period (four tokens) of the combine backward's middle part.
+__host__ __device__ __forceinline__ int64_t bwd_period_blocks(const RowArgs &a)
+{
+    return a.waves_per_token + a.dot_wpt;
+}
+
+// Workgroups of the middle part of the combine backward's grid: the periods,
+// padded to a multiple of 8 for the XCD-aware order.
 __host__ __device__ __forceinline__ int64_t bwd_mid_blocks(const RowArgs &a)
 {
     const int64_t np = (a.ndot_blocks + 7) / 8 * 8;
-    return np * (a.waves_per_token + 1);
+    return np * bwd_period_blocks(a);
 }
 
-// Grid: [sentinel blocks][periods of (waves_per_token copy blocks, 1 dot
-// block), 4 tokens each][expert blocks].
+// Grid: [sentinel blocks][periods of (waves_per_token copy blocks, dot_wpt
+// dot blocks), 4 tokens each][expert blocks].
 template <int SEG, int DSEG>
 __global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
 {
@@ -556,7 +596,7 @@ __global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
         return;
     }
     bid -= a.nsent_blocks;
-    const int64_t per = a.waves_per_token + 1;
+    const int64_t per = bwd_period_blocks(a);
     const int64_t nmid = bwd_mid_blocks(a);
     if (bid < nmid) {
         // Workgroup j is dispatched to XCD j % 8 (nsent_blocks is a multiple
@@ -568,13 +608,10 @@ __global__ void __launch_bounds__(kRowThreads) k_bwd_split(RowArgs a)
         const int64_t pos = slot % per;
         if (period >= a.ndot_blocks)
             return;
-        if (pos < a.waves_per_token) {
+        if (pos < a.waves_per_token)
             move_token<SEG>(a, period * a.waves_per_token + pos);
-        } else {
-            const int64_t t = period * kRowWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-            if (t < a.T)
-                dot_token<DSEG>(a, t, threadIdx.x & (kWave - 1));
-        }
+        else
+            dot_tokens<DSEG>(a, period * a.dot_wpt + (pos - a.waves_per_token));
         return;
     }
     fill_expert(a, static_cast<int>(bid - nmid));
@@ -834,12 +871,24 @@ static int64_t sentinel_blocks(const RowArgs &a)
     return ((pieces + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
 }
 
+static int nch_of(const RowArgs &a) { return a.H >> 3; }
+
 void row_shape(RowArgs &a)
 {
     const int whole = chunks_per_lane(a.H);
     const int cap = MOE_COPY_SEG;
-    a.dot_seg = whole < MOE_DOT_SEG ? whole : MOE_DOT_SEG;
-    // combine backward with dw: one dot workgroup per four tokens
+    // Dots: a token with about k local rows gets its row dealt over up to
+    // four waves in 1 KiB segments (more loads in flight at small T).  When
+    // the local experts are a small share of all experts (fewer than two
+    // local rows per token on uniform routing), one wave per token in 2 KiB
+    // segments does better: most dot workgroups then have little to do, and
+    // their barriers would cost more than the rows they share.
+    const bool sparse = static_cast<int64_t>(a.k) * a.EL < 2 * static_cast<int64_t>(a.E_total);
+    const int dseg = sparse ? MOE_DOT_SEG_SPARSE : MOE_DOT_SEG;
+    a.dot_seg = whole < dseg ? whole : dseg;
+    const int dnseg = (nch_of(a) + a.dot_seg * kWave - 1) / (a.dot_seg * kWave);
+    a.dot_wpt = sparse ? 1 : (dnseg >= 4 && MOE_DOT_MAX_WPT >= 4 ? 4 : (dnseg >= 2 && MOE_DOT_MAX_WPT >= 2 ? 2 : 1));
+    // combine backward with dw: periods of four tokens
     a.ndot_blocks = a.dw ? (a.T + kRowWaves - 1) / kRowWaves : 0;
     a.seg = whole < cap ? whole : cap;
     const int nch = a.H >> 3;
