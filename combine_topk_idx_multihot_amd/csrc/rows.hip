@@ -46,6 +46,19 @@
 //     landing in the next one and shortens the whole step.
 #include "moe_internal.h"
 
+// Compile-time launch parameters.  The defaults are the fastest settings
+// measured on MI355X; the others exist for measurement and give the same
+// bits, except dw, whose fp64 summation order follows the dot segmentation
+// (within the dw tolerance of the parity tests):
+//   MOE_*_SEG         KiB of a row one wave moves per segment (1, 2 or 4);
+//   MOE_MAX_WPT       most waves sharing one token's row in the row kernels;
+//   MOE_DOT_MAX_WPT   the same for the combine backward's dots;
+//   MOE_*_BATCH       rows whose loads or stores one wave keeps in flight;
+//   MOE_NT_*          non-temporal stores (zeros, copied rows) and loads
+//                     (expert-output rows of the dots);
+//   MOE_FP8_HW        E4M3 conversion by instruction (1) or bit arithmetic (0);
+//   MOE_TAIL_PIECE_KIB  KiB per wave of the sync-free tail fill.
+
 #ifndef MOE_COMBINE_SEG
 #define MOE_COMBINE_SEG 2
 #endif
@@ -91,6 +104,16 @@
 
 
 namespace moe {
+
+#define MOE_SEG_OK(x) ((x) == 1 || (x) == 2 || (x) == 4)
+static_assert(MOE_SEG_OK(MOE_COMBINE_SEG) && MOE_SEG_OK(MOE_COPY_SEG) && MOE_SEG_OK(MOE_DOT_SEG) &&
+                  MOE_SEG_OK(MOE_DOT_SEG_SPARSE),
+              "segment sizes are 1, 2 or 4 KiB");
+#undef MOE_SEG_OK
+static_assert(MOE_COPY_BATCH >= 1 && MOE_DOT_BATCH >= 1 && MOE_COMBINE_BATCH >= 1 &&
+                  MOE_DOT_BATCH <= kMaxK && MOE_COPY_BATCH <= kMaxK && MOE_COMBINE_BATCH <= kMaxK,
+              "batch sizes are 1..64 rows");
+static_assert(MOE_TAIL_PIECE_KIB >= 1, "tail pieces are at least 1 KiB");
 
 // rows whose loads (or stores) a wave keeps in flight together: dispatch and
 // FP8 dispatch (stores), the combine backward (loads of expert rows), combine
