@@ -6,7 +6,8 @@ the C entry points one for one; before passing a pointer they check that each
 tensor lives on the GPU, is contiguous, has the expected dtype and is large
 enough for what the call will write (the C ABI takes plain pointers and cannot).
 The convenience functions at the bottom (``alloc_handle``, ``route``,
-``dispatch``, ``combine``, ``combine_bwd``) only add output allocation.
+``dispatch``, ``dispatch_fp8``, ``combine``, ``combine_bwd``, ``dispatch_bwd``)
+only add output allocation.
 
 The library is loaded on first use; if it has not been built this raises
 (there is no fallback path).
