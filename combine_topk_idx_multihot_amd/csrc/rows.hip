@@ -803,10 +803,6 @@ __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
     if (t >= a.T)
         return;
     const Slots sl = load_slots(a.row_of_slot, t, a.k, a.R, lane, true);
-    // dispatch backward: a slot's weight gradient is its row's (repeated ids
-    // share the row, whose weight is the plain sum of theirs); 0 without a row
-    if (GW && c0 == 0 && lane < a.k)
-        a.grad_w[t * a.k + lane] = (sl.valid && a.grad_row_w) ? a.grad_row_w[sl.row] : 0.f;
     float acc[SEG][8];
 #pragma unroll
     for (int i = 0; i < SEG; ++i)
@@ -858,6 +854,11 @@ __global__ void __launch_bounds__(kRowThreads) k_combine(CombineArgs a)
             reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(a.out) + t * a.H)[c] = v;
         }
     }
+    // dispatch backward: a slot's weight gradient is its row's (repeated ids
+    // share the row, whose weight is the plain sum of theirs); 0 without a
+    // row.  Last, so that its load does not hold up the rows' loads.
+    if (GW && c0 == 0 && lane < a.k)
+        a.grad_w[t * a.k + lane] = (sl.valid && a.grad_row_w) ? a.grad_row_w[sl.row] : 0.f;
 }
 
 // ---------------------------------------------------------------------------
