@@ -225,6 +225,10 @@ EDGE = [
     ("k_gt_EL", 400, 32, 8, 4, 3, 2, True, 256, 0.0, False, False),
     ("empty", 0, 8, 2, 0, 8, 4, False, 256, 0.0, False, False),
     ("empty_sync_free", 0, 8, 2, 0, 8, 4, True, 256, 0.0, False, False),
+    ("max_local_1024", 700, 1024, 8, 0, 1024, 3, False, 256, 0.05, False, False),
+    ("max_local_sync_free", 300, 1500, 6, 400, 1024, 2, True, 512, 0.05, False, False),
+    ("max_k_64", 200, 100, 64, 10, 80, 2, False, 256, 0.05, False, False),
+    ("max_k_64_sync_free", 100, 64, 64, 0, 64, 1, True, 256, 0.0, False, False),
 ]
 
 
