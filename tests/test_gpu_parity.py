@@ -350,3 +350,23 @@ def test_graph_capture_replays_like_eager():
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b), rep
         _ = (x_t.float() * 2).sum().item()  # eager work between replays
+
+
+def test_eager_readback_into_pageable_host_memory():
+    """The row count also comes back when the caller's host status is pageable
+    memory (the library copies it after the kernels instead of letting the
+    kernel write it)."""
+    rng = np.random.default_rng(8)
+    T, E, k, P = 3000, 64, 6, 8
+    idx = inputs.random_routing(T, E, k, rng, p_invalid=0.1)
+    d = B.make_desc(T, k, E, pad_multiple=P)
+    h = B.alloc_handle(d)
+    h = B.Handle(desc=d, routing_map=h.routing_map, tokens_per_expert=h.tokens_per_expert,
+                 padded_offsets=h.padded_offsets, row_of_slot=h.row_of_slot, status=h.status,
+                 host_status=torch.full((4,), -9, dtype=torch.int32), workspace=h.workspace)
+    assert not h.host_status.is_pinned()
+    say("[pageable host status]")
+    B.moe_route_build(d, torch.from_numpy(idx.astype(np.int32)).cuda(), h)
+    ref = oracle.route(idx, E, P=P)
+    assert list(h.host_status.numpy()[:3]) == [ref.total, ref.flags, int(ref.tpe.sum())]
+    np.testing.assert_array_equal(h.row_of_slot.cpu().numpy(), ref.row_of_slot)
