@@ -370,3 +370,37 @@ def test_eager_readback_into_pageable_host_memory():
     ref = oracle.route(idx, E, P=P)
     assert list(h.host_status.numpy()[:3]) == [ref.total, ref.flags, int(ref.tpe.sum())]
     np.testing.assert_array_equal(h.row_of_slot.cpu().numpy(), ref.row_of_slot)
+
+
+def test_two_streams_at_once():
+    """Independent layers on two streams at the same time (the library keeps
+    no state between calls): both match the oracle."""
+    rng = np.random.default_rng(17)
+    cases = []
+    for i, (T, E, k, sf) in enumerate([(2000, 32, 4, True), (1500, 48, 6, False)]):
+        idx = inputs.random_routing(T, E, k, rng, p_invalid=0.05)
+        x = inputs.bf16_normal((T, 512), rng)
+        w = rng.random((T, k), dtype=np.float32)
+        C = oracle.capacity_min(T, k, E, 2) if sf else 0
+        d = B.make_desc(T, k, E, 0, E, 2, B.MOE_SYNC_FREE if sf else B.MOE_EAGER, False, C)
+        cases.append(dict(idx=idx, x=x, w=w, d=d, C=C, sf=sf, E=E, h=B.alloc_handle(d),
+                          s=torch.cuda.Stream(), idx_t=torch.from_numpy(idx.astype(np.int32)).cuda(),
+                          x_t=to_dev_bf16(x), w_t=torch.from_numpy(w).cuda()))
+    torch.cuda.synchronize()
+    say("[two streams]")
+    outs = []
+    for c in cases:  # both routes and dispatches queued before any result is read
+        with torch.cuda.stream(c["s"]):
+            B.moe_route_build(c["d"], c["idx_t"], c["h"], stream=c["s"])
+            R = B.rows_for(c["d"], c["h"])
+            rows, row_w, rt, re = B.dispatch(c["d"], c["h"], c["x_t"], c["w_t"], stream=c["s"])
+            out = B.combine(c["d"], c["h"], rows, stream=c["s"])
+            outs.append((rows, row_w, rt, out))
+    torch.cuda.synchronize()
+    for c, (rows, row_w, rt, out) in zip(cases, outs):
+        ref = oracle.route(c["idx"], c["E"], P=2, sync_free=c["sf"], C=c["C"], w=c["w"], x=c["x"])
+        np.testing.assert_array_equal(to_np_u16(rows), ref.rows)
+        np.testing.assert_array_equal(rt.cpu().numpy(), ref.row_token)
+        np.testing.assert_array_equal(row_w.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+        np.testing.assert_array_equal(to_np_u16(out), oracle.combine(c["idx"], ref.row_of_slot,
+                                                                     ref.rows, c["E"]))
