@@ -404,3 +404,38 @@ def test_two_streams_at_once():
         np.testing.assert_array_equal(row_w.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
         np.testing.assert_array_equal(to_np_u16(out), oracle.combine(c["idx"], ref.row_of_slot,
                                                                      ref.rows, c["E"]))
+
+
+def test_nan_inf_and_poisoned_weights():
+    """Non-finite data and poisoned weights: NaN payloads, infinities, -0 and
+    subnormals are moved bit for bit; the weights of empty and non-local slots
+    are NaN and must never reach a row; combine follows IEEE (bf16 output
+    NaNs are the canonical 0x7FC0, fp32 output compared NaN for NaN)."""
+    rng = np.random.default_rng(23)
+    T, E, k, lb, EL, H = 400, 16, 4, 4, 8, 256
+    idx = inputs.random_routing(T, E, k, rng, p_invalid=0.2)
+    x = inputs.bf16_normal((T, H), rng)
+    specials = np.array([0x7FC0, 0x7F81, 0xFFC1, 0x7F80, 0xFF80, 0x8000, 0x0001, 0x807F],
+                        np.uint16)  # qNaN, sNaN-ish, -NaN, +inf, -inf, -0, subnormals
+    pos = rng.random((T, H)) < 0.02
+    x[pos] = rng.choice(specials, size=int(pos.sum()))
+    w = rng.random((T, k), dtype=np.float32)
+    local = (idx >= lb) & (idx < lb + EL)
+    w[~local] = np.nan  # never to be read
+    g = inputs.bf16_normal((T, H), rng)
+    g[rng.random((T, H)) < 0.01] = 0x7F80
+    say("[nan/inf] dispatch, combine (bf16 and fp32), combine_bwd")
+    for f32_out in (False, True):
+        run = Run(idx, w, x, E, lb, EL, 2, grad=g, F=None, want_probs=False, f32_out=f32_out)
+        ref = oracle.route(idx, E, lb, EL, 2, w=w, x=x)
+        np.testing.assert_array_equal(run.rows, ref.rows)                   # bits, NaNs included
+        np.testing.assert_array_equal(run.row_w.view(np.uint32), ref.row_w.view(np.uint32))
+        assert not np.isnan(run.row_w).any()
+        exp = oracle.combine(idx, ref.row_of_slot, ref.rows, E, lb, EL, out="f32" if f32_out else "bf16")
+        if f32_out:
+            same = (run.out == exp) | (np.isnan(run.out) & np.isnan(exp))
+            assert same.all()
+        else:
+            np.testing.assert_array_equal(run.out, exp)
+        gr, _ = oracle.combine_bwd(idx, ref.row_of_slot, ref.row_token, g, E, lb, EL, R=ref.R)
+        np.testing.assert_array_equal(run.grad_rows, gr)
