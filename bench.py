@@ -14,15 +14,16 @@ implementation": distinct layers back to back):
     GEMM output) and the backward reads another one, F (the expert output
     before the routing weight), so no kernel of a step re-reads what an
     earlier kernel of the same step left in cache;
-  * W warm-up steps; K untimed steps with every kernel bracketed by HIP
-    events (the per-kernel breakdown, which picks the dominant kernel); then
-    the timed region: K steps between two device synchronizations, with only
-    the dominant kernel bracketed by events on its launch stream (an event
-    between every pair of kernels costs the step a few µs each).
+  * W warm-up steps; K untimed steps with every call's kernels timed (the
+    per-kernel breakdown, which picks the dominant kernel); then the timed
+    region: K steps between two device synchronizations, with only the
+    dominant call timed.  Timing is the library's moe_time_next_call with
+    fence-free events (binding.KernelTimer): the events ride on the call's own
+    kernel launches, so no event packet enters the stream.
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
-(event-timed) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
+(from its device time) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
 host on a bounded sample of the same workload.  `next` times, outside the
 step, the FP8 dispatch and the dispatch backward on the same routings.  The
 metric is quoted at 4096 and at 16384 tokens, so `also` repeats the step
@@ -170,27 +171,26 @@ def measure(name, args, with_next, torch, B, inputs):
 
     names = ("route", "dispatch", "combine", "combine_bwd")
 
-    def step(st, marks=None):
-        """One pass of the path; marks = {boundary: event} records events at
-        kernel boundaries 0 (before route) .. 4 (after combine_bwd)."""
-        m = marks or {}
-        if 0 in m:
-            m[0].record(stream)
+    def step(st, timed=None):
+        """One pass of the path; timed = {call name: KernelTimer} times those
+        calls' kernels on their own dispatch packets (no event packet enters
+        the stream)."""
+        t = timed or {}
+        if "route" in t:
+            t["route"].arm()
         B.moe_route_build(d, st["idx"], st["h"], st["w"], st["probs"], stream=stream)
         R = wl.cap if wl.sync_free else st["h"].total
-        if 1 in m:
-            m[1].record(stream)
+        if "dispatch" in t:
+            t["dispatch"].arm()
         B.moe_dispatch(d, st["h"], st["x"], H, R, st["rows"], st["w"], st["row_w"],
                        st["row_token"], st["row_expert"], stream=stream)
-        if 2 in m:
-            m[2].record(stream)
+        if "combine" in t:
+            t["combine"].arm()
         B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)
-        if 3 in m:
-            m[3].record(stream)
+        if "combine_bwd" in t:
+            t["combine_bwd"].arm()
         B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["F"], st["dw"],
                           stream=stream)
-        if 4 in m:
-            m[4].record(stream)
         return R
 
     for i in range(args.warmup):
@@ -210,38 +210,36 @@ def measure(name, args, with_next, torch, B, inputs):
         facts.append(byte_model(wl, int(hs[2]), R, n_active, 4, True)
                      | byte_model_next(wl, int(hs[2]), R, n_active) | {"R": R})
 
-    # breakdown pass (untimed): every kernel bracketed by events; picks the
-    # dominant kernel.  Events between all kernels cost the step a few µs
-    # each, so the timed region below brackets only the dominant one.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # breakdown pass (untimed): every call's kernels timed; picks the
+    # dominant kernel
+    evs = [{n: B.KernelTimer(stream) for n in names} for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
-        step(sets[i % len(sets)], dict(enumerate(evs[i])))
+        step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
     kern = {}
-    for j, n in enumerate(names):
-        ms = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+    for n in names:
+        ms = [evs[i][n].elapsed_ms() for i in range(args.steps)]
         b = float(np.mean([facts[i % len(sets)][n] for i in range(args.steps)]))
         avg = float(np.mean(ms))
         kern[n] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),
                    "alg_bytes": int(b), "GBps": round(b / (avg * 1e-3) / 1e9, 1)}
     dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda n: kern[n]["avg_us"])
-    jd = names.index(dominant)
 
     # timed region: K steps between two synchronizations; the dominant
-    # kernel's launches bracketed by events on the launch stream
-    dev_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(args.steps)]
+    # call's kernels timed live on their launch stream
+    dev_ = [B.KernelTimer(stream) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % len(sets)], {jd: dev_[i][0], jd + 1: dev_[i][1]})
+        step(sets[i % len(sets)], {dominant: dev_[i]})
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     step_bytes = float(np.mean([sum(facts[i % len(sets)][n] for n in names)
                                 for i in range(args.steps)]))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in dev_]))
+    dom_ms = float(np.mean([t.elapsed_ms() for t in dev_]))
     dom_bytes = float(np.mean([facts[i % len(sets)][dominant] for i in range(args.steps)]))
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     dev_us = sum(kern[n]["avg_us"] for n in names)
@@ -281,7 +279,8 @@ def measure(name, args, with_next, torch, B, inputs):
 
 def time_next(wl, d, sets, facts, steps, stream, torch, B, kern):
     """The FP8 dispatch and the dispatch backward over the same buffer sets
-    (handles as routed by the step), each launch bracketed by HIP events."""
+    (handles as routed by the step), each call's kernels timed by the library
+    (moe_time_next_call)."""
     H, T, k = wl.H, wl.T, wl.k
     dev = sets[0]["x"].device
     gen = torch.Generator(device=dev)
@@ -298,27 +297,25 @@ def time_next(wl, d, sets, facts, steps, stream, torch, B, kern):
         st, f = sets[i % len(sets)], facts[i % len(sets)]
         R = f["R"]
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].arm()
         B.moe_dispatch_fp8(d, st["h"], st["x"], H, R, st["rows_q"], st["row_scale"], st["w"],
                            st["row_w"], st["row_token"], st["row_expert"], stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].arm()
         # grad rows: the F buffer (independent of every other input here)
         B.moe_dispatch_bwd(d, st["h"], st["F"], H, R, st["grad_x"], st["grad_row_w"],
                            st["grad_topk_w"], stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(2):
         run(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [(B.KernelTimer(stream), B.KernelTimer(stream)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         run(i, evs[i])
     torch.cuda.synchronize()
     out = {}
     for j, n in enumerate(("dispatch_fp8", "dispatch_bwd")):
-        ms = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]
+        ms = [evs[i][j].elapsed_ms() for i in range(steps)]
         b = float(np.mean([facts[i % len(sets)][n] for i in range(steps)]))
         avg = float(np.mean(ms))
         out[n] = {"avg_us": round(avg * 1e3, 2), "median_us": round(float(np.median(ms)) * 1e3, 2),

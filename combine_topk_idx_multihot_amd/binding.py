@@ -31,7 +31,7 @@ MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
 # Every symbol include/moe_mi355x.h declares.
 EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build", "moe_dispatch",
            "moe_dispatch_fp8", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
-           "moe_last_error", "moe_device_check")
+           "moe_last_error", "moe_device_check", "moe_time_next_call")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_device_check.argtypes = [ctypes.c_int]
         L.moe_device_check.restype = ctypes.c_int
+        L.moe_time_next_call.argtypes = [vp, vp]
+        L.moe_time_next_call.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -332,6 +334,88 @@ def moe_dispatch_bwd(desc: Desc, handle: Handle, grad_rows: torch.Tensor, H: int
 
 def moe_device_check(device: int = 0) -> int:
     return _check(lib().moe_device_check(device))
+
+
+def _event(ev) -> int | None:
+    if ev is None:
+        return None
+    if isinstance(ev, torch.cuda.Event):
+        if not ev.cuda_event:
+            raise MoeError(MOE_ERR_ARG, "the torch event has no HIP event yet: record it once first")
+        return ev.cuda_event
+    return int(ev)
+
+
+def moe_time_next_call(start_event=None, stop_event=None) -> int:
+    """The next library call on this thread times its kernels into the two
+    events (torch.cuda.Event with enable_timing=True, recorded once so that
+    its HIP event exists, or raw hipEvent_t handles)."""
+    return _check(lib().moe_time_next_call(_event(start_event), _event(stop_event)))
+
+
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hip_runtime_api.h
+
+
+class KernelTimer:
+    """Two HIP events for moe_time_next_call, created with
+    hipEventDisableSystemFence: events used only for timing need no
+    system-scope cache write-back when they complete, which otherwise delays
+    the next kernel by a few microseconds.  The events come from the HIP
+    runtime the library itself is linked against.
+
+        t = KernelTimer(stream)
+        t.arm(); B.moe_combine_bwd(...)       # the next call is timed
+        torch.cuda.synchronize(); t.elapsed_ms()
+    """
+
+    def __init__(self, stream=None):
+        L = lib()
+        if not getattr(L, "_timer_protos", False):
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            L._timer_protos = True
+        self._L = L
+        self.start = self._create()
+        self.stop = self._create()
+        s = _stream(stream)
+        for e in (self.start, self.stop):  # so that elapsed_ms is defined from the start
+            self._hip(L.hipEventRecord(e, s), "hipEventRecord")
+
+    def _hip(self, rc, what):
+        if rc != 0:
+            raise MoeError(MOE_ERR_HIP, f"{what} failed with HIP error {rc}")
+
+    def _create(self):
+        e = ctypes.c_void_p()
+        self._hip(self._L.hipEventCreateWithFlags(ctypes.byref(e), _HIP_EVENT_DISABLE_SYSTEM_FENCE),
+                  "hipEventCreateWithFlags")
+        return e.value
+
+    def arm(self):
+        """Time the kernels of the next library call made on this thread."""
+        _check(self._L.moe_time_next_call(self.start, self.stop))
+
+    def elapsed_ms(self) -> float:
+        """Device time of the timed call's kernels; valid once they are done."""
+        f = ctypes.c_float()
+        self._hip(self._L.hipEventElapsedTime(ctypes.byref(f), self.start, self.stop),
+                  "hipEventElapsedTime")
+        return f.value
+
+    def close(self):
+        for name in ("start", "stop"):
+            e = self.__dict__.pop(name, None)
+            if e:
+                self._L.hipEventDestroy(e)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---------------------------------------------------------------------------

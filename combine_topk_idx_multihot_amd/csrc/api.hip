@@ -22,6 +22,12 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Drops the calling thread's timing request when an entry point returns, so
+// that a request applies to one call only.
+struct TimingScope {
+    ~TimingScope() { moe::launch_timing() = moe::LaunchTiming{}; }
+};
+
 int fail(int code, const char *fmt, ...)
 {
     va_list ap;
@@ -227,6 +233,7 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
                     float *multihot_probs, const moe_handle *handle, int32_t *host_status,
                     void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
@@ -314,6 +321,7 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
                  const float *topk_w, int64_t R, uint16_t *rows, float *row_w, int32_t *row_token,
                  int32_t *row_expert, void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_dispatch(desc, handle, x, H, topk_w, R, row_w)) != MOE_OK)
         return rc;
@@ -327,6 +335,7 @@ int moe_dispatch_fp8(const moe_desc *desc, const moe_handle *handle, const uint1
                      const float *topk_w, int64_t R, uint8_t *rows_q, float *row_scale,
                      float *row_w, int32_t *row_token, int32_t *row_expert, void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_dispatch(desc, handle, x, H, topk_w, R, row_w)) != MOE_OK)
         return rc;
@@ -342,6 +351,7 @@ int moe_dispatch_fp8(const moe_desc *desc, const moe_handle *handle, const uint1
 int moe_combine(const moe_desc *desc, const moe_handle *handle, const uint16_t *Y, int32_t H,
                 int64_t R, void *out, int32_t out_is_f32, void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
@@ -381,6 +391,7 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
                     const uint16_t *expert_out, int32_t H, int64_t R, uint16_t *grad_rows,
                     float *dw, void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
@@ -434,6 +445,7 @@ int moe_dispatch_bwd(const moe_desc *desc, const moe_handle *handle, const uint1
                      int32_t H, int64_t R, const float *grad_row_w, void *grad_x,
                      int32_t grad_x_is_f32, float *grad_topk_w, void *stream)
 {
+    TimingScope timing_scope;
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
@@ -475,6 +487,14 @@ int moe_dispatch_bwd(const moe_desc *desc, const moe_handle *handle, const uint1
 
 const char *moe_last_error(void) { return g_err; }
 
+int moe_time_next_call(void *start_event, void *stop_event)
+{
+    moe::LaunchTiming &t = moe::launch_timing();
+    t.start = static_cast<hipEvent_t>(start_event);
+    t.stop = static_cast<hipEvent_t>(stop_event);
+    return ok();
+}
+
 int moe_device_check(int device)
 {
     int n = 0;
@@ -493,3 +513,11 @@ int moe_device_check(int device)
 }
 
 }  // extern "C"
+
+namespace moe {
+LaunchTiming &launch_timing()
+{
+    thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace moe

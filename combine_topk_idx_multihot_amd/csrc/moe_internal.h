@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/moe_mi355x.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -99,5 +100,29 @@ struct CombineArgs {
 // Combine; with grad_w set it is also the dispatch backward (the weight
 // gradients of the slots are gathered from their rows).
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+
+// Kernel timing request of the calling host thread (moe_time_next_call).
+// The events ride on the kernels' own dispatch packets: the first kernel of
+// the next entry point records `start`, and every kernel of it re-records
+// `stop`, so the pair spans that call's kernels with no packet between them.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming &launch_timing();
+
+// Every kernel of the library is launched through this.
+template <typename A>
+inline void launch(void (*kernel)(A), dim3 grid, dim3 block, size_t lds, hipStream_t s, const A &arg)
+{
+    LaunchTiming &t = launch_timing();
+    if (t.start || t.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), s, t.start, t.stop,
+                              0u, arg);
+        t.start = nullptr;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, arg);
+    }
+}
 
 }  // namespace moe

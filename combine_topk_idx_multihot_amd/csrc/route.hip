@@ -446,22 +446,22 @@ hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
     if (a.nblk > 0) {
         const size_t lds = count_lds_bytes(threads, a.EL);
         if (a.idx_i64)
-            k_route_count<int64_t><<<dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s>>>(a);
+            launch(k_route_count<int64_t>, dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s, a);
         else
-            k_route_count<int32_t><<<dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s>>>(a);
+            launch(k_route_count<int32_t>, dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s, a);
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }
     if (a.nblk > 0 && a.nblk * a.EL <= kFusedFinishMax) {
-        k_route_finish<<<dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s>>>(a);
+        launch(k_route_finish, dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
-    k_route_scan<<<dim3(1), dim3(1024), 0, s>>>(a);
+    launch(k_route_scan, dim3(1), dim3(1024), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess)
         return err;
     const int64_t nslots = a.T * a.k;
     if (nslots > 0) {
-        k_route_rows<<<dim3(static_cast<unsigned>((nslots + 255) / 256)), dim3(256), 0, s>>>(a);
+        launch(k_route_rows, dim3(static_cast<unsigned>((nslots + 255) / 256)), dim3(256), 0, s, a);
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }

@@ -937,7 +937,7 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
         return hipErrorInvalidConfiguration;
     if (!a0.eager && a0.nsent_blocks > 0) {
         // sync-free: the tail first, on its own, then the rows
-        k_sentinel_oneshot<<<dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s>>>(a0);
+        launch(k_sentinel_oneshot, dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s, a0);
         a.nsent_blocks = 0;
     }
     const int64_t nmid = a.dw ? bwd_mid_blocks(a) : a.ntok_blocks;
@@ -948,27 +948,27 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
     const dim3 blk(kRowThreads);
     if (a.rows_q) {
         switch (a.seg) {
-        case 1: k_dispatch_fp8<1><<<g, blk, 0, s>>>(a); break;
-        case 2: k_dispatch_fp8<2><<<g, blk, 0, s>>>(a); break;
-        default: k_dispatch_fp8<4><<<g, blk, 0, s>>>(a); break;
+        case 1: launch(k_dispatch_fp8<1>, g, blk, 0, s, a); break;
+        case 2: launch(k_dispatch_fp8<2>, g, blk, 0, s, a); break;
+        default: launch(k_dispatch_fp8<4>, g, blk, 0, s, a); break;
         }
     } else if (a.dw) {
         switch (a.seg * 8 + a.dot_seg) {
-        case 1 * 8 + 1: k_bwd_split<1, 1><<<g, blk, 0, s>>>(a); break;
-        case 1 * 8 + 2: k_bwd_split<1, 2><<<g, blk, 0, s>>>(a); break;
-        case 1 * 8 + 4: k_bwd_split<1, 4><<<g, blk, 0, s>>>(a); break;
-        case 2 * 8 + 1: k_bwd_split<2, 1><<<g, blk, 0, s>>>(a); break;
-        case 2 * 8 + 2: k_bwd_split<2, 2><<<g, blk, 0, s>>>(a); break;
-        case 2 * 8 + 4: k_bwd_split<2, 4><<<g, blk, 0, s>>>(a); break;
-        case 4 * 8 + 1: k_bwd_split<4, 1><<<g, blk, 0, s>>>(a); break;
-        case 4 * 8 + 2: k_bwd_split<4, 2><<<g, blk, 0, s>>>(a); break;
-        default: k_bwd_split<4, 4><<<g, blk, 0, s>>>(a); break;
+        case 1 * 8 + 1: launch(k_bwd_split<1, 1>, g, blk, 0, s, a); break;
+        case 1 * 8 + 2: launch(k_bwd_split<1, 2>, g, blk, 0, s, a); break;
+        case 1 * 8 + 4: launch(k_bwd_split<1, 4>, g, blk, 0, s, a); break;
+        case 2 * 8 + 1: launch(k_bwd_split<2, 1>, g, blk, 0, s, a); break;
+        case 2 * 8 + 2: launch(k_bwd_split<2, 2>, g, blk, 0, s, a); break;
+        case 2 * 8 + 4: launch(k_bwd_split<2, 4>, g, blk, 0, s, a); break;
+        case 4 * 8 + 1: launch(k_bwd_split<4, 1>, g, blk, 0, s, a); break;
+        case 4 * 8 + 2: launch(k_bwd_split<4, 2>, g, blk, 0, s, a); break;
+        default: launch(k_bwd_split<4, 4>, g, blk, 0, s, a); break;
         }
     } else {
         switch (a.seg) {
-        case 1: k_move_rows<1><<<g, blk, 0, s>>>(a); break;
-        case 2: k_move_rows<2><<<g, blk, 0, s>>>(a); break;
-        default: k_move_rows<4><<<g, blk, 0, s>>>(a); break;
+        case 1: launch(k_move_rows<1>, g, blk, 0, s, a); break;
+        case 2: launch(k_move_rows<2>, g, blk, 0, s, a); break;
+        default: launch(k_move_rows<4>, g, blk, 0, s, a); break;
         }
     }
     return hipGetLastError();
@@ -978,9 +978,9 @@ template <bool F32, bool GW>
 static void launch_comb(int seg, dim3 g, const CombineArgs &a, hipStream_t s)
 {
     switch (seg) {
-    case 1: k_combine<1, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    case 2: k_combine<2, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
-    default: k_combine<4, F32, GW><<<g, dim3(kRowThreads), 0, s>>>(a); break;
+    case 1: launch(k_combine<1, F32, GW>, g, dim3(kRowThreads), 0, s, a); break;
+    case 2: launch(k_combine<2, F32, GW>, g, dim3(kRowThreads), 0, s, a); break;
+    default: launch(k_combine<4, F32, GW>, g, dim3(kRowThreads), 0, s, a); break;
     }
 }
 

@@ -239,6 +239,25 @@ const char *moe_last_error(void);
  * Does not launch anything. */
 int moe_device_check(int device);
 
+/* Kernel timing, for callers that measure the library (a benchmark, a
+ * profiler hook).  The next moe_route_build, moe_dispatch, moe_dispatch_fp8,
+ * moe_combine, moe_combine_bwd or moe_dispatch_bwd call made on this host
+ * thread times its own kernels into two HIP events:
+ *   start_event  hipEvent_t (created by the caller, timing enabled) or NULL:
+ *                takes the start time of the call's first kernel.
+ *   stop_event   hipEvent_t or NULL: takes the end time of the call's last
+ *                kernel.
+ * hipEventElapsedTime(start, stop) then gives the device time of that call's
+ * kernels.  The events are attached to the kernels' own dispatch packets, so
+ * unlike hipEventRecord around the call they add no packet, and no gap, to
+ * the stream.  Events created with hipEventDisableSystemFence suit this use
+ * best: without it, each event's completion writes back the caches at system
+ * scope, which delays the next kernel by a few microseconds.
+ * The request is dropped when that call returns, whether or not
+ * it launched anything (a call that fails or has nothing to launch leaves the
+ * events as they were).  Events stay owned by the caller.  Returns MOE_OK. */
+int moe_time_next_call(void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

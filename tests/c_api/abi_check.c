@@ -8,7 +8,8 @@
  * then combine is the identity on every token with a valid id, and zero on the
  * others; the checks below are that identity, the counts against a host
  * histogram, the padded offsets, the row of every slot, the sync-free tail,
- * the dispatch backward and the error path for a bad hidden size.
+ * the dispatch backward, the error path for a bad hidden size, and the
+ * dispatch's device time from moe_time_next_call.
  * Prints "abi ok" and exits 0 on success.
  */
 #include <stdint.h>
@@ -119,6 +120,11 @@ static int run(int sync_free)
     int32_t *d_rt = dev(sizeof(int32_t) * R);
     int32_t *d_re = dev(sizeof(int32_t) * R);
     float *d_out = dev(sizeof(float) * T * H);
+    /* the dispatch timed through its own launches */
+    hipEvent_t ev0, ev1;
+    HIPCHECK(hipEventCreateWithFlags(&ev0, hipEventDisableSystemFence));
+    HIPCHECK(hipEventCreateWithFlags(&ev1, hipEventDisableSystemFence));
+    CHECK(moe_time_next_call(ev0, ev1) == MOE_OK);
     CHECK(moe_dispatch(&d, &hd, d_x, H, d_w, R, d_rows, d_row_w, d_rt, d_re, NULL) == MOE_OK);
     CHECK(moe_combine(&d, &hd, d_rows, H, R, d_out, 1, NULL) == MOE_OK);
     /* dispatch backward of (grad rows = the rows, grad row weights = row weights) */
@@ -128,6 +134,11 @@ static int run(int sync_free)
     /* a bad hidden size is rejected before any launch */
     CHECK(moe_combine(&d, &hd, d_rows, 100, R, d_out, 1, NULL) == MOE_ERR_HIDDEN);
     HIPCHECK(hipDeviceSynchronize());
+    float disp_ms = 0.0f;
+    HIPCHECK(hipEventElapsedTime(&disp_ms, ev0, ev1));
+    CHECK(disp_ms > 0.0f && disp_ms < 1000.0f);
+    HIPCHECK(hipEventDestroy(ev0));
+    HIPCHECK(hipEventDestroy(ev1));
 
     int32_t *ros = malloc(sizeof(int32_t) * T);
     int32_t *rt = malloc(sizeof(int32_t) * R);
@@ -181,8 +192,8 @@ static int run(int sync_free)
             for (int h = 0; h < H; ++h)
                 CHECK(rows[(size_t)r * H + h] == 0);
 
-    printf("%s: T=%d E=%d H=%d rows=%lld total=%d\n", sync_free ? "sync-free" : "eager", T, E, H,
-           (long long)R, st[0]);
+    printf("%s: T=%d E=%d H=%d rows=%lld total=%d dispatch %.1f us\n",
+           sync_free ? "sync-free" : "eager", T, E, H, (long long)R, st[0], disp_ms * 1e3f);
     free(idx); free(w); free(x); free(ros); free(rt); free(re); free(rw); free(rows); free(out);
     free(gx); free(gtw);
     hipFree(hd.routing_map); hipFree(hd.tokens_per_expert); hipFree(hd.padded_offsets);
