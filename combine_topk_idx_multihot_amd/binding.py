@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from dataclasses import dataclass
 
 import torch
@@ -412,6 +413,8 @@ class KernelTimer:
                 self._L.hipEventDestroy(e)
 
     def __del__(self):
+        if sys.is_finalizing():  # the HIP runtime may already be torn down
+            return
         try:
             self.close()
         except Exception:
