@@ -1,0 +1,86 @@
+"""bench.py's host logic on the CPU: the one-GPU guard, and the algorithmic
+byte model held against the HBM traffic the hardware counters measured.
+
+profiles/traffic.json holds rocprofv3 FETCH_SIZE / WRITE_SIZE per launch of
+every call on the four measured layers, scaled by a plain copy of known size.
+The byte model counts each input once and each output once.  The row kernels
+re-read and over-write nothing, so the two must agree closely; a mistake in
+the model (a dropped metadata array, rows counted for the wrong R, the FP8
+scales forgotten) shows up as a mismatch of several percent.  The routing facts
+(data rows, padded rows, active tokens) come from the same seeded generators
+the benchmark uses.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from combine_topk_idx_multihot_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROW_CALLS = ("dispatch", "combine", "combine_bwd", "dispatch_bwd", "dispatch_fp8")
+
+
+def traffic():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as fh:
+        return json.load(fh)
+
+
+def routing_facts(wl, seed):
+    """(data rows, rows R, tokens with a local slot) of one seeded routing."""
+    idx, _ = inputs.make_routing(wl, seed)
+    lb, EL = wl.lb, wl.num_local
+    tpe = np.array([(idx == lb + e).any(axis=1).sum() for e in range(EL)], np.int64)
+    data = int(tpe.sum())
+    R = wl.cap if wl.sync_free else int(((tpe + wl.P - 1) // wl.P * wl.P).sum())
+    n_active = int(((idx >= lb) & (idx < lb + EL)).any(axis=1).sum())
+    return data, R, n_active
+
+
+def model_bytes(wname, sets=4):
+    """The benchmark's byte model averaged over its buffer sets (same seeds)."""
+    wl = inputs.WORKLOADS[wname]
+    seed0 = 1000 + list(inputs.WORKLOADS).index(wname) + 1
+    acc = {}
+    for s in range(sets):
+        data, R, n_active = routing_facts(wl, seed0 + 7919 * s)
+        m = bench.byte_model(wl, data, R, n_active, 4, True) | bench.byte_model_next(wl, data, R,
+                                                                                   n_active)
+        for k, v in m.items():
+            acc[k] = acc.get(k, 0.0) + v / sets
+    return acc
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr
+
+
+@pytest.mark.parametrize("wname", sorted(traffic()["workloads"]))
+def test_byte_model_matches_counted_traffic(wname):
+    meas = traffic()["workloads"][wname]
+    model = model_bytes(wname)
+    for call in ROW_CALLS:
+        ratio = meas[call]["bytes"] / model[call]
+        # the row kernels: within 2.5 % (measured 1.000 to 1.021)
+        assert abs(ratio - 1.0) <= 0.025, (wname, call, ratio)
+    # the route's two passes hand the packed slot ranks and the per-block
+    # counts through memory, which the model does not count: measured 1.10 to
+    # 1.24 times the model, a few MB at most
+    r = meas["route"]["bytes"] / model["route"]
+    assert 1.0 <= r <= 1.3, (wname, r)
+
+
+def test_traffic_is_null_once_sources_change(monkeypatch):
+    t = traffic()
+    w = next(iter(t["workloads"]))
+    if t["source_sha256"] == bench.kernel_source_sha256():
+        assert bench.measured_traffic(w, "combine_bwd") == int(t["workloads"][w]["combine_bwd"]["bytes"])
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
+    assert bench.measured_traffic(w, "combine_bwd") is None
