@@ -20,6 +20,9 @@ implementation": distinct layers back to back):
     dominant call timed.  Timing is the library's moe_time_next_call with
     fence-free events (binding.KernelTimer): the events ride on the call's own
     kernel launches, so no event packet enters the stream.
+  * the dispatch, which follows the eager readback on the step's critical
+    path, goes through binding.PreparedDispatch: the set's buffers (sized for
+    the worst case) are checked once, and each step passes its row count.
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
@@ -166,6 +169,11 @@ def measure(name, args, with_next, torch, B, inputs):
             "probs": torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev),
             "h": B.alloc_handle(d, dev),
         }
+        # the dispatch right after the eager readback is on the step's critical
+        # path: its buffers are checked once, and each step passes only R
+        st["dispatch"] = B.PreparedDispatch(d, st["h"], st["x"], H, st["rows"], st["w"],
+                                            st["row_w"], st["row_token"], st["row_expert"],
+                                            stream=stream)
         sets.append(st)
     torch.cuda.synchronize()
 
@@ -182,8 +190,7 @@ def measure(name, args, with_next, torch, B, inputs):
         R = wl.cap if wl.sync_free else st["h"].total
         if "dispatch" in t:
             t["dispatch"].arm()
-        B.moe_dispatch(d, st["h"], st["x"], H, R, st["rows"], st["w"], st["row_w"],
-                       st["row_token"], st["row_expert"], stream=stream)
+        st["dispatch"](R)
         if "combine" in t:
             t["combine"].arm()
         B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)

@@ -273,6 +273,48 @@ def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, ro
                                      p_rw, p_rt, p_re, _stream(stream)))
 
 
+class PreparedDispatch:
+    """moe_dispatch over buffers that a loop reuses on every step, checked once.
+
+    For eager loops whose row buffers are sized for the worst case (for
+    instance moe_capacity_min rows): each call passes only the step's row count
+    R (the host total from that step's moe_route_build) and fills rows [0, R).
+    The Python-side checks of moe_dispatch are made here once, against the
+    buffers' capacity, which takes them off the path between the eager
+    readback and the dispatch launch; the library still checks every argument
+    on every call.  The tensors must stay as they are (no resize_ or set_)
+    while the object is in use; it holds references to them.
+    """
+
+    def __init__(self, desc: Desc, handle: Handle, x: torch.Tensor, H: int, rows: torch.Tensor,
+                 topk_w: torch.Tensor | None = None, row_w: torch.Tensor | None = None,
+                 row_token: torch.Tensor | None = None, row_expert: torch.Tensor | None = None,
+                 stream=None):
+        if H <= 0 or rows is None:
+            raise MoeError(MOE_ERR_ARG, "H must be positive and rows given")
+        cap = rows.numel() // H
+        if cap == 0:
+            raise MoeError(MOE_ERR_ARG, "rows holds no [H] row")
+        if (topk_w is None) != (row_w is None):
+            raise MoeError(MOE_ERR_ARG, "topk_w and row_w go together")
+        p_x = _dev(x, "x", _BF16, desc.T * H) if desc.T else None
+        p_rows = _dev(rows, "rows", _BF16, cap * H)
+        p_w = _dev(topk_w, "topk_w", _F32, desc.T * desc.k, optional=True) if desc.T else None
+        p_rw = _dev(row_w, "row_w", _F32, cap, optional=True) if p_w is not None else None
+        p_rt = _dev(row_token, "row_token", _I32, cap, optional=True)
+        p_re = _dev(row_expert, "row_expert", _I32, cap, optional=True)
+        self.capacity = cap
+        self._fn = lib().moe_dispatch
+        self._head = (ctypes.byref(desc), handle.cref(), p_x, H, p_w)
+        self._tail = (p_rows, p_rw, p_rt, p_re, _stream(stream))
+        self._keep = (desc, handle, x, rows, topk_w, row_w, row_token, row_expert)
+
+    def __call__(self, R: int) -> int:
+        if not 0 <= R <= self.capacity:
+            raise MoeError(MOE_ERR_ARG, f"R={R} outside [0, {self.capacity}] rows of the buffers")
+        return _check(self._fn(*self._head, R, *self._tail))
+
+
 def moe_dispatch_fp8(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int,
                      rows_q: torch.Tensor, row_scale: torch.Tensor,
                      topk_w: torch.Tensor | None = None, row_w: torch.Tensor | None = None,
