@@ -305,9 +305,12 @@ class PreparedDispatch:
         p_re = _dev(row_expert, "row_expert", _I32, cap, optional=True)
         self.capacity = cap
         self._fn = lib().moe_dispatch
-        self._head = (ctypes.byref(desc), handle.cref(), p_x, H, p_w)
+        # a private copy: the checks above hold for this descriptor, whatever
+        # later becomes of the caller's
+        self._desc = Desc.from_buffer_copy(desc)
+        self._head = (ctypes.byref(self._desc), handle.cref(), p_x, H, p_w)
         self._tail = (p_rows, p_rw, p_rt, p_re, _stream(stream))
-        self._keep = (desc, handle, x, rows, topk_w, row_w, row_token, row_expert)
+        self._keep = (handle, x, rows, topk_w, row_w, row_token, row_expert)
 
     def __call__(self, R: int) -> int:
         if not 0 <= R <= self.capacity:
