@@ -202,3 +202,29 @@ def test_dispatch_bwd_argument_rules():
     assert dbwd_rc(d, gw=FAKE, gtw=None) == B.MOE_ERR_ARG   # weights given, nowhere to go
     assert dbwd_rc(d, gw=None, gtw=FAKE) == B.MOE_ERR_ARG   # weight grads without input
     assert "grad" in B.last_error()
+
+
+def test_error_messages_are_per_thread():
+    """moe_last_error belongs to the calling thread: a failure in another
+    thread leaves this thread's message alone, and a new thread starts with
+    none."""
+    import threading
+
+    L = B.lib()
+    good = B.make_desc(100, 2, 8)
+    assert L.moe_route_workspace_size(ctypes.byref(good)) > 0
+    bad = B.make_desc(100, 0, 8)  # k = 0
+    before = B.last_error()
+    seen = {}
+
+    def other():
+        seen["fresh"] = B.last_error()
+        seen["size"] = L.moe_route_workspace_size(ctypes.byref(bad))
+        seen["msg"] = B.last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["fresh"] == ""
+    assert seen["size"] == 0 and "k must be" in seen["msg"]
+    assert B.last_error() == before
