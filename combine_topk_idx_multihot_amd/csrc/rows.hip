@@ -23,11 +23,12 @@
 //     of a batch of rows (8 for combine, 4 for the dots) before consuming any
 //     of them.
 //   * the combine backward is the dispatch of grad_out plus, in workgroups of
-//     their own interleaved with the copying ones, the fp64 dots of grad_out
-//     with the expert-output rows of the token's slots: one wave per token
-//     walks the row and keeps its partial dots in registers, a butterfly
-//     over the wave ends each dot, so dw is the same on every run and no
-//     wave waits for another.
+//     their own interleaved with the copying ones, the dots of grad_out with
+//     the expert-output rows of the token's slots.  A token's row is dealt
+//     over 1 to 4 dot waves; each keeps its exact bf16 x bf16 products summed
+//     in fp64 registers, a butterfly ends each wave's part, and the token's
+//     first wave adds the parts in wave order through LDS before the single
+//     rounding to fp32, so dw is the same on every run.
 //   * pad rows are zeroed by extra workgroups of the rows' launch (one per
 //     expert).  The sync-free tail [total, R) -- most of the bytes when the
 //     worst case is far from the routed total -- is a launch of its own just
@@ -477,9 +478,9 @@ __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
     zero_rows(a, r0, r1, wave, a.nsent_blocks * kRowWaves, threadIdx.x & (kWave - 1));
 }
 
-// Grid: [sentinel blocks][token blocks][expert blocks].  The sentinel tail
-// (all of the worst-case rows past total) is the longest-running part in
-// sync-free mode, so its workgroups are dispatched first.
+// Grid: [sentinel blocks][token blocks][expert blocks].  Sentinel blocks are
+// eager mode's few workgroups for the (normally empty) [total, R); in
+// sync-free mode the tail has a launch of its own and there are none here.
 template <int SEG>
 __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 {
@@ -875,9 +876,9 @@ static int chunks_per_lane(int H)
     return n;
 }
 
-// Sentinel-fill workgroups: sync-free mode sizes them for the whole
-// worst-case tail, about four 64 KiB zero tasks per wave; eager mode keeps a
-// handful for the (normally empty) [total, R).
+// Sentinel-fill workgroups: in sync-free mode, those of the tail's own
+// launch, one piece per wave over the whole worst-case row array; eager mode
+// keeps a handful in the rows' launch for the (normally empty) [total, R).
 static int64_t sentinel_blocks(const RowArgs &a)
 {
     // always a multiple of 8, so that the workgroups after them keep their
