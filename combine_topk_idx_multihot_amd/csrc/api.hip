@@ -149,6 +149,10 @@ int check_rows(const moe_desc *d, int64_t R)
 
 int hip_fail(hipError_t e, const char *what)
 {
+    // the launchers' own refusal of a grid past 2^32 work-items (no HIP call made)
+    if (e == hipErrorInvalidConfiguration)
+        return fail(MOE_ERR_ARG, "%s: the problem is too large for one launch (its grid would pass "
+                                 "2^32 work-items)", what);
     return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 

@@ -8,15 +8,17 @@
 
 namespace moe {
 
-// Largest grid (x) dimension a launch may use; launches that would need more
-// return hipErrorInvalidConfiguration instead of truncating the count.
-constexpr int64_t kMaxGrid = 2147483647;
-
 constexpr int kWave = 64;
 constexpr int kMaxK = 64;         // slots per token handled lane-parallel by one wave
 constexpr int kMaxLocal = 1024;   // local experts (LDS bitmap bound)
 constexpr int kRowWaves = 4;      // waves per workgroup in the row kernels
 constexpr int kRowThreads = kRowWaves * kWave;
+
+// A kernel dispatch packet carries the grid size in work-items as a 32-bit
+// number, so a row launch takes at most this many workgroups; the launchers
+// return hipErrorInvalidConfiguration, before any launch, for a problem that
+// would need more (a row array past 64 GiB, for instance).
+constexpr int64_t kMaxRowBlocks = 0xFFFFFFFFll / kRowThreads;
 
 // Launch geometry of the routing-count kernel: one workgroup covers
 // tokens_per_block whole tokens (k slots each, one thread per slot).

@@ -934,7 +934,9 @@ __global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
 hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
 {
     RowArgs a = a0;
-    if (a0.nsent_blocks + a0.ntok_blocks + a0.nexp_blocks + bwd_mid_blocks(a0) > kMaxGrid)
+    // the sync-free tail's launch and the rows' launch, each within the limit
+    if (a0.nsent_blocks > kMaxRowBlocks ||
+        a0.nsent_blocks + a0.ntok_blocks + a0.nexp_blocks + bwd_mid_blocks(a0) > kMaxRowBlocks)
         return hipErrorInvalidConfiguration;
     if (!a0.eager && a0.nsent_blocks > 0) {
         // sync-free: the tail first, on its own, then the rows
@@ -994,7 +996,7 @@ hipError_t launch_combine(const CombineArgs &a, hipStream_t s)
     const int64_t nb = (a.T * nseg + kRowWaves - 1) / kRowWaves;
     if (nb == 0)
         return hipSuccess;
-    if (nb > kMaxGrid)
+    if (nb > kMaxRowBlocks)
         return hipErrorInvalidConfiguration;
     const dim3 g(static_cast<unsigned>(nb));
     const bool gw = a.grad_w != nullptr;

@@ -26,7 +26,10 @@
  *     row pointer must be 16-byte aligned.
  *   - Return value is a moe_status; on failure moe_last_error() names the
  *     violated requirement.  Argument errors are detected on the host before
- *     anything is launched.  Nothing throws.
+ *     anything is launched.  Nothing throws.  A problem too large for one
+ *     launch (a kernel grid past 2^32 work-items, which the dispatch packet
+ *     cannot hold: row arrays past about 64 GiB) is one such error,
+ *     MOE_ERR_ARG.
  *   - Only MOE_EAGER moe_route_build waits for the device (once, to read the
  *     row count back: "Eager vs captured").  Every other call, and every call in
  *     MOE_SYNC_FREE mode, is asynchronous, allocation-free and safe to record

@@ -228,3 +228,22 @@ def test_error_messages_are_per_thread():
     assert seen["fresh"] == ""
     assert seen["size"] == 0 and "k must be" in seen["msg"]
     assert B.last_error() == before
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="fake device pointers: run where nothing can be launched")
+def test_grids_past_2_32_work_items_are_refused():
+    """A kernel dispatch packet holds the grid size in work-items as a 32-bit
+    number.  A problem whose launch would need more is refused before any
+    launch, with MOE_ERR_ARG and a message that says why."""
+    # sync-free, 2^30 rows of H = 65536: the tail launch alone would need
+    # 2^37 one-KiB pieces
+    C = 1 << 30
+    d = _desc(T=1000, k=2, E=8, num_local=8, pad_multiple=1, mode=B.MOE_SYNC_FREE, capacity=C)
+    assert dispatch_rc(d, H=65536, R=C) == B.MOE_ERR_ARG
+    assert "too large for one launch" in B.last_error()
+    assert bwd_rc(d, H=65536, R=C) == B.MOE_ERR_ARG
+    # 2^27 tokens of H = 65536 to combine: 2^31 workgroups
+    d = _desc(T=1 << 27, k=1, E=8, num_local=8, pad_multiple=1)
+    assert combine_rc(d, H=65536, R=10) == B.MOE_ERR_ARG
+    assert "too large for one launch" in B.last_error()
