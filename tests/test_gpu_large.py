@@ -34,7 +34,7 @@ def test_rows_past_4gib():
     idx = inputs.random_routing(T, E, k, rng, p_invalid=0.05)
     w = rng.random((T, k), dtype=np.float32)
     C = oracle.capacity_min(T, k, E, P)
-    assert C * H * 2 > (1 << 32) + (1 << 30), C
+    assert C * H * 2 > (1 << 32) + (1 << 29), C  # well past 4 GiB
     say(f"[large] sync-free T={T} k={k} E={E} P={P} H={H} C={C}: "
         f"{C * H * 2 / 1e9:.2f} GB per row array")
     gen = torch.Generator(device="cuda")
@@ -81,8 +81,8 @@ def test_rows_past_4gib():
     want_g[tok < 0] = 0
     np.testing.assert_array_equal(rows_np(grad_rows, sample), want_g)
     # the zero tail, whole (a device-side reduction over 0.26 GB per array)
-    assert int(rows[total:].view(torch.int16).abs().amax()) == 0
-    assert int(grad_rows[total:].view(torch.int16).abs().amax()) == 0
+    assert not bool((rows[total:].view(torch.int16) != 0).any())
+    assert not bool((grad_rows[total:].view(torch.int16) != 0).any())
 
     # combine and the combine backward of the sampled tokens, from the oracle
     # on the compact sub-problem (rows U renumbered 0..|U|-1)
