@@ -7,7 +7,9 @@ with the oracle.  The rows and grad rows are compared on samples: rows around
 the 4 GiB boundary, around the routed total, the last rows, random rows, and
 the rows of sampled tokens.  For the sampled tokens, the oracle computes the
 combine and the combine backward (grad rows and dw) on the compact
-sub-problem they make up.  The zero tail is checked whole on the device.
+sub-problem they make up.  The zero tail is checked whole on the device.  The
+FP8 dispatch of the same layer is checked the same way; its E4M3 rows are H
+bytes, so the same boundary row starts at byte 2^31 of the code array.
 """
 import numpy as np
 import pytest
@@ -101,3 +103,24 @@ def test_rows_past_4gib():
     check_dw(dw.cpu().numpy()[S], dw_c, idx[S], ros_c, g_S, F_c, 0, E, E)
     say(f"  total={total}, {len(sample)} rows and {len(S)} tokens sampled, "
         f"{int((U >= BOUNDARY_ROW).sum())} of their rows past 4 GiB")
+
+    # the FP8 dispatch of the same layer: E4M3 rows of H bytes, so the same
+    # boundary row starts at byte 2^31 of the code array
+    del grad_rows, F
+    q, sc, rw8, rt8, re8 = B.dispatch_fp8(d, h, x, w_t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(rt8.cpu().numpy(), ref.row_token)
+    np.testing.assert_array_equal(re8.cpu().numpy(), ref.row_expert)
+    np.testing.assert_array_equal(rw8.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+    sel = torch.from_numpy(sample.astype(np.int64)).cuda()
+    q_s = q.view(torch.uint8).index_select(0, sel).cpu().numpy()
+    sc_s = sc.index_select(0, sel).cpu().numpy()
+    data = tok >= 0
+    toks = np.unique(tok[data])
+    compact = np.searchsorted(toks, tok[data]).astype(np.int32)
+    q_exp, s_exp = oracle.dispatch_fp8(rows_np(x, toks), compact)
+    np.testing.assert_array_equal(q_s[data], q_exp)
+    np.testing.assert_array_equal(sc_s[data].view(np.uint32), s_exp.view(np.uint32))
+    assert not q_s[~data].any() and not sc_s[~data].any()
+    assert not bool((q.view(torch.uint8)[total:] != 0).any())
+    assert not bool((sc[total:] != 0).any())
