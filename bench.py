@@ -20,9 +20,12 @@ implementation": distinct layers back to back):
     dominant call timed.  Timing is the library's moe_time_next_call with
     fence-free events (binding.KernelTimer): the events ride on the call's own
     kernel launches, so no event packet enters the stream.
-  * the dispatch, which follows the eager readback on the step's critical
-    path, goes through binding.PreparedDispatch: the set's buffers (sized for
-    the worst case) are checked once, and each step passes its row count.
+  * eager steps route and dispatch in one call (moe_route_dispatch) into the
+    set's worst-case-sized buffers: the dispatch is queued before the row
+    count is read back, so the device does not wait for the host between the
+    two.  The per-kernel breakdown times the route and the dispatch as two
+    calls (the same kernels on the same inputs); sync-free steps always use two
+    calls, with the dispatch through binding.PreparedDispatch.
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
@@ -184,13 +187,21 @@ def measure(name, args, with_next, torch, B, inputs):
         calls' kernels on their own dispatch packets (no event packet enters
         the stream)."""
         t = timed or {}
-        if "route" in t:
-            t["route"].arm()
-        B.moe_route_build(d, st["idx"], st["h"], st["w"], st["probs"], stream=stream)
-        R = wl.cap if wl.sync_free else st["h"].total
-        if "dispatch" in t:
-            t["dispatch"].arm()
-        st["dispatch"](R)
+        if wl.sync_free or "route" in t or "dispatch" in t:
+            # two calls: sync-free never waits, and the breakdown times each
+            if "route" in t:
+                t["route"].arm()
+            B.moe_route_build(d, st["idx"], st["h"], st["w"], st["probs"], stream=stream)
+            R = wl.cap if wl.sync_free else st["h"].total
+            if "dispatch" in t:
+                t["dispatch"].arm()
+            st["dispatch"](R)
+        else:
+            # eager: one call, whose dispatch is queued before the readback
+            B.moe_route_dispatch(d, st["idx"], st["h"], st["x"], H, st["rows"], st["w"],
+                                 st["probs"], st["row_w"], st["row_token"], st["row_expert"],
+                                 stream=stream)
+            R = st["h"].total
         if "combine" in t:
             t["combine"].arm()
         B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)

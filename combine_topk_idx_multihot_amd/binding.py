@@ -30,7 +30,8 @@ MOE_EAGER, MOE_SYNC_FREE = 0, 1
 MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
 
 # Every symbol include/moe_mi355x.h declares.
-EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build", "moe_dispatch",
+EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build",
+           "moe_route_dispatch", "moe_dispatch",
            "moe_dispatch_fp8", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
            "moe_last_error", "moe_device_check", "moe_time_next_call")
 
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_device_check.argtypes = [ctypes.c_int]
         L.moe_device_check.restype = ctypes.c_int
+        L.moe_route_dispatch.argtypes = [pd, vp, vp, vp, ph, vp, vp, i32, i64, vp, vp, vp, vp, vp]
+        L.moe_route_dispatch.restype = ctypes.c_int
         L.moe_time_next_call.argtypes = [vp, vp]
         L.moe_time_next_call.restype = ctypes.c_int
         _lib = L
@@ -251,6 +254,32 @@ def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle,
     href = handle.cref()
     return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, href,
                                         handle.host_status.data_ptr(), _stream(stream)))
+
+
+def moe_route_dispatch(desc: Desc, topk_idx: torch.Tensor, handle: Handle, x: torch.Tensor,
+                       H: int, rows: torch.Tensor, topk_w: torch.Tensor | None = None,
+                       multihot_probs: torch.Tensor | None = None,
+                       row_w: torch.Tensor | None = None, row_token: torch.Tensor | None = None,
+                       row_expert: torch.Tensor | None = None, stream=None) -> int:
+    """Eager route and dispatch in one call, into buffers of R_cap =
+    rows.shape[0] >= moe_capacity_min rows; the dispatch is queued before the
+    row count is read back.  Returns MOE_OK; handle.total is then the count,
+    and rows [0, total) are filled."""
+    T, k = desc.T, desc.k
+    R_cap = rows.numel() // H if H > 0 else 0
+    p_idx = _dev(topk_idx, "topk_idx", _I64 if desc.idx_is_i64 else _I32, T * k) if T * k else None
+    p_w = _dev(topk_w, "topk_w", _F32, T * k, optional=True) if T else None
+    p_probs = _dev(multihot_probs, "multihot_probs", _F32, T * desc.E, optional=True)
+    p_x = _dev(x, "x", _BF16, T * H) if T else None
+    p_rows = _dev(rows, "rows", _BF16, R_cap * H) if R_cap else None
+    p_rw = _dev(row_w, "row_w", _F32, R_cap, optional=True)
+    p_rt = _dev(row_token, "row_token", _I32, R_cap, optional=True)
+    p_re = _dev(row_expert, "row_expert", _I32, R_cap, optional=True)
+    if p_w is None:
+        p_rw = None if T == 0 else p_rw
+    return _check(lib().moe_route_dispatch(ctypes.byref(desc), p_idx, p_w, p_probs, handle.cref(),
+                                           handle.host_status.data_ptr(), p_x, H, R_cap, p_rows,
+                                           p_rw, p_rt, p_re, _stream(stream)))
 
 
 def moe_dispatch(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int, rows: torch.Tensor,

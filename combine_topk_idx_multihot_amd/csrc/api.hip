@@ -184,9 +184,10 @@ int check_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_
 int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
                     const float *topk_w, int64_t R, uint16_t *rows, uint8_t *rows_q,
                     float *row_scale, float *row_w, int32_t *row_token, int32_t *row_expert,
-                    void *stream)
+                    void *stream, bool keep_tail = false)
 {
     moe::RowArgs a;
+    a.keep_tail = keep_tail;
     a.src = x;
     a.topk_w = topk_w;
     a.F = nullptr;
@@ -233,11 +234,15 @@ size_t moe_route_workspace_size(const moe_desc *desc)
     return ws_layout(desc).bytes;
 }
 
-int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                    float *multihot_probs, const moe_handle *handle, int32_t *host_status,
-                    void *stream)
+}  // extern "C"
+
+namespace {
+
+// The route's checks and launches.  `a` keeps what route_wait needs.
+int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                 void *stream, moe::RouteArgs &a)
 {
-    TimingScope timing_scope;
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
@@ -256,7 +261,6 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
     char *workspace = static_cast<char *>(handle->workspace);
 
     const moe::RouteGeom g = moe::route_geom(desc->T, desc->k, desc->num_local);
-    moe::RouteArgs a;
     a.idx = topk_idx;
     a.w = topk_w;
     a.probs = multihot_probs;
@@ -287,38 +291,116 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
         else
             (void)hipGetLastError(); // an unregistered pointer is not an error here
     }
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    volatile int32_t *hs = host_status;
     if (a.host_status)
-        hs[3] = -1; // turned to 0 by the kernel once words 0..2 are written
-    hipError_t e = moe::launch_route(a, g.threads, s);
+        static_cast<volatile int32_t *>(host_status)[3] = -1; // the kernel turns it to 0 last
+    hipError_t e = moe::launch_route(a, g.threads, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, "route launch");
-    if (desc->mode == MOE_EAGER) {
-        // "Eager vs captured": the counts come back to the host once.  With a
-        // device-visible status the host waits only for that word (a bounded
-        // spin, then a stream sync); the rest of the route runs on, ordered
-        // before whatever the caller queues next on the stream.
-        bool ready = false;
-        if (a.host_status) {
-            const auto t0 = std::chrono::steady_clock::now();
-            while (!(ready = (hs[3] == 0))) {
-                _mm_pause();
-                if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(5))
-                    break;
-            }
-        } else if ((e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
-                                       hipMemcpyDeviceToHost, s)) != hipSuccess) {
-            return hip_fail(e, "status readback");
+    return MOE_OK;
+}
+
+// Eager mode: "Eager vs captured" -- the counts come back to the host once.
+// With a device-visible status the host waits only for that word (a bounded
+// spin, then a stream sync); the rest of the route, and whatever was queued
+// after it, runs on.  Pageable memory takes a copy and a stream sync.
+int route_wait(const moe_handle *handle, int32_t *host_status, void *stream,
+               const moe::RouteArgs &a)
+{
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    volatile int32_t *hs = host_status;
+    hipError_t e;
+    bool ready = false;
+    if (a.host_status) {
+        const auto t0 = std::chrono::steady_clock::now();
+        while (!(ready = (hs[3] == 0))) {
+            _mm_pause();
+            if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(5))
+                break;
         }
-        if (!ready && (e = hipStreamSynchronize(s)) != hipSuccess)
-            return hip_fail(e, "stream sync");
-        if (host_status[1] & MOE_FLAG_BAD_ID)
-            return fail(MOE_ERR_INDEX, "an expert id outside [-1, E=%d) was seen; such slots were "
-                                       "treated as empty", desc->E);
+    } else if ((e = hipMemcpyAsync(host_status, handle->status, 4 * sizeof(int32_t),
+                                   hipMemcpyDeviceToHost, s)) != hipSuccess) {
+        return hip_fail(e, "status readback");
     }
-    return ok();
+    if (!ready && (e = hipStreamSynchronize(s)) != hipSuccess)
+        return hip_fail(e, "stream sync");
+    return MOE_OK;
+}
+
+// Eager mode's report of out-of-range ids, from the status read back.
+int bad_id_check(const moe_desc *desc, const int32_t *host_status)
+{
+    if (host_status[1] & MOE_FLAG_BAD_ID)
+        return fail(MOE_ERR_INDEX, "an expert id outside [-1, E=%d) was seen; such slots were "
+                                   "treated as empty", desc->E);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                    float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                    void *stream)
+{
+    TimingScope timing_scope;
+    moe::RouteArgs a;
+    int rc = route_launch(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream, a);
+    if (rc == MOE_OK && desc->mode == MOE_EAGER) {
+        if ((rc = route_wait(handle, host_status, stream, a)) == MOE_OK)
+            rc = bad_id_check(desc, host_status);
+    }
+    return rc == MOE_OK ? ok() : rc;
+}
+
+int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                       float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                       const uint16_t *x, int32_t H, int64_t R_cap, uint16_t *rows, float *row_w,
+                       int32_t *row_token, int32_t *row_expert, void *stream)
+{
+    TimingScope timing_scope;
+    int rc;
+    // every argument of both halves is checked before anything is launched
+    if ((rc = check_desc(desc)) != MOE_OK)
+        return rc;
+    if (desc->mode != MOE_EAGER)
+        return fail(MOE_ERR_ARG, "moe_route_dispatch is for eager mode (sync-free calls never wait: "
+                                 "queue moe_route_build and moe_dispatch)");
+    if ((rc = check_handle(desc, handle, true)) != MOE_OK)
+        return rc;
+    if ((rc = check_hidden(H)) != MOE_OK)
+        return rc;
+    if (R_cap < cap_min(desc) || R_cap > kI32Max)
+        return fail(MOE_ERR_CAPACITY, "R_cap %lld must hold the worst case T*min(k,EL) + EL*(P-1) = "
+                                      "%lld rows (and fit in int32)",
+                    (long long)R_cap, (long long)cap_min(desc));
+    if (desc->T > 0 && (!x || !aligned16(x)))
+        return fail(MOE_ERR_ARG, "x must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
+    if (R_cap > 0 && (!rows || !aligned16(rows)))
+        return fail(MOE_ERR_ARG, "rows must be a non-NULL, 16-byte aligned [R_cap,H] bf16 tensor");
+    if ((multihot_probs || row_w) && !topk_w)
+        return fail(MOE_ERR_ARG, "multihot_probs or row_w requested without topk_w");
+    if (topk_w && !multihot_probs && !row_w)
+        return fail(MOE_ERR_ARG, "topk_w given but neither multihot_probs nor row_w is requested");
+    if (!host_status)
+        return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
+
+    moe::RouteArgs a;
+    if ((rc = route_launch(desc, topk_idx, multihot_probs ? topk_w : nullptr, multihot_probs, handle,
+                           host_status, stream, a)) != MOE_OK)
+        return rc;
+    // pageable status: its copy (and sync) go ahead of the dispatch
+    if (!a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
+        return rc;
+    // the dispatch, queued before the row count is known: bounded by the
+    // buffers' capacity, it writes the rows [0, total) and leaves the rest
+    if ((rc = launch_dispatch(desc, handle, x, H, row_w ? topk_w : nullptr, R_cap, rows, nullptr,
+                              nullptr, row_w, row_token, row_expert, stream, true)) != MOE_OK)
+        return rc;
+    if (a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
+        return rc;
+    rc = bad_id_check(desc, host_status);
+    return rc == MOE_OK ? ok() : rc;
 }
 
 int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,

@@ -76,6 +76,8 @@ struct RowArgs {
     int32_t dot_wpt;           // combine backward: waves sharing one token's dots (1, 2 or 4)
     int64_t ntok_blocks, nexp_blocks, nsent_blocks;
     int64_t ndot_blocks;       // combine backward with dw: periods of 4 tokens, 0 otherwise
+    int32_t keep_tail = 0;     // eager, R = the buffers' capacity: rows past the total are
+                               // left as they are (no sentinel fill)
 };
 
 // Row movement: dispatch (x -> rows, or with rows_q set x -> E4M3 rows and

@@ -883,6 +883,8 @@ static int64_t sentinel_blocks(const RowArgs &a)
 {
     // always a multiple of 8, so that the workgroups after them keep their
     // index modulo the XCD count
+    if (a.keep_tail)
+        return 0;
     if (a.eager)
         return 8;
     // sync-free: the tail's own launch, one piece per wave over the whole row

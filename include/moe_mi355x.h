@@ -162,6 +162,36 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
                  int32_t *row_token, int32_t *row_expert, void *stream);
 
 /*
+ * Eager route and dispatch in one call ("Eager vs captured": the eager mode's
+ * one readback, taken off the device's critical path).  For callers whose
+ * row buffers hold the worst case, moe_capacity_min(desc) rows, such as a
+ * loop over persistent buffers.  The dispatch is queued right behind the
+ * route, before the row count is read back.  So the device goes from the
+ * route to the dispatch without waiting for the host, while the host waits
+ * for the count as moe_route_build does.
+ *   desc.mode      MOE_EAGER (sync-free calls never wait: use the two calls).
+ *   topk_idx, multihot_probs, handle, host_status: as for moe_route_build.
+ *   topk_w         device [T,k] fp32 or NULL: read for multihot_probs and for
+ *                  row_w, and needed by either.
+ *   x, H           as for moe_dispatch.
+ *   R_cap          rows the buffers hold, >= moe_capacity_min(desc), else
+ *                  MOE_ERR_CAPACITY.
+ *   rows           device [R_cap,H] bf16 out; row_w, row_token, row_expert:
+ *                  device [R_cap] out or NULL.
+ * On return host_status holds {total, flags, data rows} as after
+ * moe_route_build, and rows [0, total) of every output are exactly what
+ * moe_dispatch with R = total writes.  Rows at or past total are not
+ * written.  Every argument of both halves is checked before anything is
+ * launched.  An out-of-range id returns MOE_ERR_INDEX after the readback, as
+ * moe_route_build does; the dispatch has then still run, with such slots
+ * treated as empty.
+ */
+int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                       float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                       const uint16_t *x, int32_t H, int64_t R_cap, uint16_t *rows, float *row_w,
+                       int32_t *row_token, int32_t *row_expert, void *stream);
+
+/*
  * FP8 dispatch ("What this adds": FP8 dispatch, named there as a follow-up
  * that halves the dispatched bytes; the page fixes no format, this library
  * takes the following one).  As moe_dispatch, except that each row holds the

@@ -247,3 +247,29 @@ def test_grids_past_2_32_work_items_are_refused():
     d = _desc(T=1 << 27, k=1, E=8, num_local=8, pad_multiple=1)
     assert combine_rc(d, H=65536, R=10) == B.MOE_ERR_ARG
     assert "too large for one launch" in B.last_error()
+
+
+def rd_rc(d, H=2048, R_cap=None, idx=FAKE, w=None, probs=None, host=FAKE, x=FAKE, rows=FAKE,
+          row_w=None):
+    h = _handle()
+    R_cap = B.lib().moe_capacity_min(ctypes.byref(d)) if R_cap is None else R_cap
+    return B.lib().moe_route_dispatch(ctypes.byref(d), idx, w, probs, ctypes.byref(h), host, x, H,
+                                      R_cap, rows, row_w, None, None, None)
+
+
+def test_route_dispatch_argument_rules():
+    """The eager route-and-dispatch checks the arguments of both halves before
+    it launches anything."""
+    d = _desc()
+    cap = B.lib().moe_capacity_min(ctypes.byref(d))
+    sf = _desc(mode=B.MOE_SYNC_FREE, capacity=cap)
+    assert rd_rc(sf) == B.MOE_ERR_ARG and "eager" in B.last_error()
+    assert rd_rc(d, R_cap=cap - 1) == B.MOE_ERR_CAPACITY
+    assert rd_rc(d, H=384) == B.MOE_ERR_HIDDEN
+    assert rd_rc(d, host=None) == B.MOE_ERR_ARG
+    assert rd_rc(d, x=None) == B.MOE_ERR_ARG
+    assert rd_rc(d, rows=FAKE + 8) == B.MOE_ERR_ARG
+    assert rd_rc(d, row_w=FAKE) == B.MOE_ERR_ARG        # row weights without topk_w
+    assert rd_rc(d, probs=FAKE) == B.MOE_ERR_ARG        # probs without topk_w
+    assert rd_rc(d, w=FAKE) == B.MOE_ERR_ARG            # weights with nothing to write
+    assert rd_rc(_desc(k=0)) == B.MOE_ERR_ARG

@@ -1,0 +1,124 @@
+"""moe_route_dispatch on the GPU: the eager route and dispatch in one call,
+with the dispatch queued before the row count is read back.
+
+It is held against moe_route_build followed by moe_dispatch with R = total.
+These must match bit for bit: the handle's metadata, the host status, the
+multihot probs, and rows [0, total) of every dispatch output.  Rows at or past
+the total must keep what the buffers held before.  The cases cover pinned and
+pageable host status, ragged and padded routing, out-of-range ids (the call
+returns MOE_ERR_INDEX after the readback, and the dispatch has run with those
+slots empty), one token, and no tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_topk_idx_multihot_amd import binding as B
+from combine_topk_idx_multihot_amd import inputs
+from test_gpu_parity import gpu, say  # noqa: F401 (gpu: fixture)
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (label, T, E, k, lb, EL, P, H, p_invalid, p_bad, pinned)
+    ("qwen_like", 4096, 128, 8, 0, 128, 16, 2048, 0.0, 0.0, True),
+    ("ragged_padded", 1027, 40, 6, 4, 30, 7, 768, 0.1, 0.0, True),
+    ("pageable_status", 999, 32, 4, 0, 32, 3, 512, 0.05, 0.0, False),
+    ("bad_ids", 500, 16, 4, 0, 16, 2, 256, 0.1, 0.05, True),
+    ("one_token", 1, 8, 4, 2, 5, 4, 256, 0.0, 0.0, True),
+    ("no_tokens", 0, 8, 2, 0, 8, 4, 256, 0.0, 0.0, True),
+]
+
+
+def handle_for(d, pinned):
+    h = B.alloc_handle(d)
+    if not pinned:
+        h = B.Handle(desc=d, routing_map=h.routing_map, tokens_per_expert=h.tokens_per_expert,
+                     padded_offsets=h.padded_offsets, row_of_slot=h.row_of_slot, status=h.status,
+                     host_status=torch.zeros(4, dtype=torch.int32), workspace=h.workspace)
+    return h
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_route_dispatch_matches_two_calls(case):
+    label, T, E, k, lb, EL, P, H, p_inv, p_bad, pinned = case
+    say(f"[route_dispatch] {label} T={T} E={E} k={k} lb={lb} EL={EL} P={P} H={H} pinned={pinned}")
+    rng = np.random.default_rng([31, T, E, k, EL, P])
+    idx = inputs.random_routing(T, E, k, rng, p_invalid=p_inv, p_out_of_range=p_bad)
+    d = B.make_desc(T, k, E, lb, EL, P, B.MOE_EAGER, False, 0)
+    cap = B.moe_capacity_min(d)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    w = torch.rand((T, k), device="cuda")
+    x = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+
+    # reference: the two calls
+    h1 = handle_for(d, pinned)
+    probs1 = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    rc1 = B.MOE_OK
+    try:
+        B.moe_route_build(d, idx_t, h1, w, probs1)
+    except B.MoeError as e:
+        rc1 = e.code
+    R = int(h1.host_status[0])
+    ref = B.dispatch(d, h1, x, w)
+    torch.cuda.synchronize()
+
+    # one call, into buffers of the worst case holding a marker
+    h2 = handle_for(d, pinned)
+    probs2 = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    rows = torch.full((cap, H), -3.0, dtype=torch.bfloat16, device="cuda")
+    row_w = torch.full((cap,), -5.0, device="cuda")
+    rt = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    re = torch.full((cap,), -9, dtype=torch.int32, device="cuda")
+    rc2 = B.MOE_OK
+    try:
+        B.moe_route_dispatch(d, idx_t, h2, x, H, rows, w, probs2, row_w, rt, re)
+    except B.MoeError as e:
+        rc2 = e.code
+    torch.cuda.synchronize()
+
+    assert rc1 == rc2 == (B.MOE_ERR_INDEX if p_bad > 0 else B.MOE_OK)
+    assert h2.host_status.tolist()[:3] == h1.host_status.tolist()[:3]
+    assert int(h2.host_status[0]) == R
+    for name in ("routing_map", "tokens_per_expert", "padded_offsets", "row_of_slot", "status"):
+        assert torch.equal(getattr(h1, name), getattr(h2, name)), name
+    assert torch.equal(probs1.view(torch.int32), probs2.view(torch.int32))
+    assert torch.equal(rows[:R], ref[0])
+    assert torch.equal(row_w[:R].view(torch.int32), ref[1].view(torch.int32))
+    assert torch.equal(rt[:R], ref[2])
+    assert torch.equal(re[:R], ref[3])
+    # rows past the total are not written
+    assert bool((rows[R:] == -3.0).all()) and bool((row_w[R:] == -5.0).all())
+    assert bool((rt[R:] == -7).all()) and bool((re[R:] == -9).all())
+    say(f"  total={R} of {cap} rows")
+
+
+def test_route_dispatch_timed_and_repeated():
+    """The call under a timing request spans the route and the dispatch, and
+    repeated calls through one handle give the same rows every time."""
+    T, E, k, P, H = 2048, 64, 8, 16, 1024
+    rng = np.random.default_rng(5)
+    idx = inputs.random_routing(T, E, k, rng)
+    d = B.make_desc(T, k, E, 0, E, P, B.MOE_EAGER, False, 0)
+    cap = B.moe_capacity_min(d)
+    h = B.alloc_handle(d)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).cuda()
+    w = torch.rand((T, k), device="cuda")
+    x = torch.randn((T, H), device="cuda").to(torch.bfloat16)
+    rows = torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")
+    row_w = torch.empty(cap, device="cuda")
+    B.moe_route_dispatch(d, idx_t, h, x, H, rows, w, None, row_w)
+    R = h.total
+    first = rows[:R].clone()
+    timer = B.KernelTimer()
+    torch.cuda.synchronize()
+    for i in range(5):
+        if i == 2:
+            timer.arm()
+        B.moe_route_dispatch(d, idx_t, h, x, H, rows, w, None, row_w)
+        assert h.total == R
+    torch.cuda.synchronize()
+    assert torch.equal(rows[:R], first)
+    ms = timer.elapsed_ms()
+    say(f"[route_dispatch] timed call: {ms * 1e3:.1f} us (route and dispatch)")
+    assert 0.0 < ms < 10.0
