@@ -8,8 +8,9 @@
  * then combine is the identity on every token with a valid id, and zero on the
  * others; the checks below are that identity, the counts against a host
  * histogram, the padded offsets, the row of every slot, the sync-free tail,
- * the dispatch backward, the error path for a bad hidden size, and the
- * dispatch's device time from moe_time_next_call.
+ * the dispatch backward, the error path for a bad hidden size, the
+ * dispatch's device time from moe_time_next_call, and (eager) the same route
+ * and dispatch as one moe_route_dispatch call into worst-case buffers.
  * Prints "abi ok" and exits 0 on success.
  */
 #include <stdint.h>
@@ -191,6 +192,29 @@ static int run(int sync_free)
         if (rt[r] < 0)
             for (int h = 0; h < H; ++h)
                 CHECK(rows[(size_t)r * H + h] == 0);
+
+    /* eager: the same route and dispatch as one call into worst-case buffers
+       gives the same rows [0, total) and leaves the rest as it was */
+    if (!sync_free) {
+        const int64_t cap = moe_capacity_min(&d);
+        CHECK(cap >= R);
+        uint16_t *d_rows2 = dev(sizeof(uint16_t) * cap * H);
+        float *d_rw2 = dev(sizeof(float) * cap);
+        HIPCHECK(hipMemset(d_rows2, 0xAB, sizeof(uint16_t) * cap * H));
+        CHECK(moe_route_dispatch(&d, d_idx, d_w, NULL, &hd, host_status, d_x, H, cap, d_rows2,
+                                 d_rw2, NULL, NULL, NULL) == MOE_OK);
+        CHECK(host_status[0] == R);
+        uint16_t *rows2 = malloc(sizeof(uint16_t) * cap * H);
+        float *rw2 = malloc(sizeof(float) * cap);
+        HIPCHECK(hipMemcpy(rows2, d_rows2, sizeof(uint16_t) * cap * H, hipMemcpyDeviceToHost));
+        HIPCHECK(hipMemcpy(rw2, d_rw2, sizeof(float) * cap, hipMemcpyDeviceToHost));
+        CHECK(memcmp(rows2, rows, sizeof(uint16_t) * R * H) == 0);
+        CHECK(memcmp(rw2, rw, sizeof(float) * R) == 0);
+        for (int64_t i = R * H; i < cap * H; ++i)
+            CHECK(rows2[i] == 0xABAB);
+        free(rows2); free(rw2);
+        hipFree(d_rows2); hipFree(d_rw2);
+    }
 
     printf("%s: T=%d E=%d H=%d rows=%lld total=%d dispatch %.1f us\n",
            sync_free ? "sync-free" : "eager", T, E, H, (long long)R, st[0], disp_ms * 1e3f);
