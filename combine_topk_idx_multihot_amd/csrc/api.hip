@@ -181,10 +181,12 @@ int check_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_
 }
 
 // One launch of the dispatch: bf16 rows, or (rows_q set) E4M3 rows and scales.
-int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
-                    const float *topk_w, int64_t R, uint16_t *rows, uint8_t *rows_q,
-                    float *row_scale, float *row_w, int32_t *row_token, int32_t *row_expert,
-                    void *stream, bool keep_tail = false)
+// The arguments and launch shape of one dispatch: bf16 rows, or (rows_q set)
+// E4M3 rows and scales.
+moe::RowArgs dispatch_args(const moe_desc *desc, const moe_handle *handle, const uint16_t *x,
+                           int32_t H, const float *topk_w, int64_t R, uint16_t *rows,
+                           uint8_t *rows_q, float *row_scale, float *row_w, int32_t *row_token,
+                           int32_t *row_expert, bool keep_tail)
 {
     moe::RowArgs a;
     a.keep_tail = keep_tail;
@@ -210,6 +212,17 @@ int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
     moe::row_shape(a);
+    return a;
+}
+
+// One launch of the dispatch.
+int launch_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t *x, int32_t H,
+                    const float *topk_w, int64_t R, uint16_t *rows, uint8_t *rows_q,
+                    float *row_scale, float *row_w, int32_t *row_token, int32_t *row_expert,
+                    void *stream)
+{
+    const moe::RowArgs a = dispatch_args(desc, handle, x, H, topk_w, R, rows, rows_q, row_scale,
+                                         row_w, row_token, row_expert, false);
     hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(e, rows_q ? "fp8 dispatch launch" : "dispatch launch");
@@ -384,6 +397,12 @@ int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *
         return fail(MOE_ERR_ARG, "topk_w given but neither multihot_probs nor row_w is requested");
     if (!host_status)
         return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
+    // the dispatch, bounded by the buffers' capacity: it writes the rows
+    // [0, total) and leaves the rest
+    const moe::RowArgs ra = dispatch_args(desc, handle, x, H, row_w ? topk_w : nullptr, R_cap, rows,
+                                          nullptr, nullptr, row_w, row_token, row_expert, true);
+    if (!moe::move_rows_fits(ra))
+        return hip_fail(hipErrorInvalidConfiguration, "dispatch");
 
     moe::RouteArgs a;
     if ((rc = route_launch(desc, topk_idx, multihot_probs ? topk_w : nullptr, multihot_probs, handle,
@@ -392,11 +411,10 @@ int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *
     // pageable status: its copy (and sync) go ahead of the dispatch
     if (!a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
         return rc;
-    // the dispatch, queued before the row count is known: bounded by the
-    // buffers' capacity, it writes the rows [0, total) and leaves the rest
-    if ((rc = launch_dispatch(desc, handle, x, H, row_w ? topk_w : nullptr, R_cap, rows, nullptr,
-                              nullptr, row_w, row_token, row_expert, stream, true)) != MOE_OK)
-        return rc;
+    // the dispatch, queued before the row count is known
+    hipError_t e = moe::launch_move_rows(ra, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(e, "dispatch launch");
     if (a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
         return rc;
     rc = bad_id_check(desc, host_status);

@@ -86,6 +86,7 @@ struct RowArgs {
 // row_shape fills in the launch shape (segment size, waves per token, block
 // counts) from the other fields.
 void row_shape(RowArgs &a);
+bool move_rows_fits(const RowArgs &a); // launch_move_rows' grids within kMaxRowBlocks
 hipError_t launch_move_rows(const RowArgs &a, hipStream_t s);
 
 struct CombineArgs {

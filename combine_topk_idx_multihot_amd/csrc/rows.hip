@@ -933,12 +933,17 @@ __global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
     fill_sentinel_oneshot(a, blockIdx.x);
 }
 
+bool move_rows_fits(const RowArgs &a)
+{
+    // the sync-free tail's launch and the rows' launch, each within the limit
+    return a.nsent_blocks <= kMaxRowBlocks &&
+           a.nsent_blocks + a.ntok_blocks + a.nexp_blocks + bwd_mid_blocks(a) <= kMaxRowBlocks;
+}
+
 hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
 {
     RowArgs a = a0;
-    // the sync-free tail's launch and the rows' launch, each within the limit
-    if (a0.nsent_blocks > kMaxRowBlocks ||
-        a0.nsent_blocks + a0.ntok_blocks + a0.nexp_blocks + bwd_mid_blocks(a0) > kMaxRowBlocks)
+    if (!move_rows_fits(a0))
         return hipErrorInvalidConfiguration;
     if (!a0.eager && a0.nsent_blocks > 0) {
         // sync-free: the tail first, on its own, then the rows

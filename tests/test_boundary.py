@@ -247,6 +247,9 @@ def test_grids_past_2_32_work_items_are_refused():
     d = _desc(T=1 << 27, k=1, E=8, num_local=8, pad_multiple=1)
     assert combine_rc(d, H=65536, R=10) == B.MOE_ERR_ARG
     assert "too large for one launch" in B.last_error()
+    # the eager route-and-dispatch refuses before it launches the route
+    assert rd_rc(d, H=65536) == B.MOE_ERR_ARG
+    assert "too large for one launch" in B.last_error()
 
 
 def rd_rc(d, H=2048, R_cap=None, idx=FAKE, w=None, probs=None, host=FAKE, x=FAKE, rows=FAKE,
