@@ -29,7 +29,8 @@ implementation": distinct layers back to back):
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
-(from its device time) against MI355X's 8 TB/s; `cpu_baseline` times the oracle on the
+(from its device time) against MI355X's 8 TB/s, and against the HIP runtime's
+1 GiB device copy timed on the same box (`hip_copy_GBps`, `frac_of_hip_copy`); `cpu_baseline` times the oracle on the
 host on a bounded sample of the same workload.  `next` times, outside the
 step, the FP8 dispatch and the dispatch backward on the same routings.  The
 metric is quoted at 4096 and at 16384 tokens, so `also` repeats the step
@@ -117,6 +118,10 @@ def main():
 
     B.moe_device_check(0)
     result, sets, wl = measure(args.workload, args, not args.no_next, torch, B, inputs)
+    # beside the 8 TB/s peak: the HIP runtime's own device copy on this machine
+    ceil = copy_ceiling(torch, torch.cuda.current_stream())
+    result["roofline"]["hip_copy_GBps"] = round(ceil, 1)
+    result["roofline"]["frac_of_hip_copy"] = round(result["roofline"]["achieved"] / ceil, 4)
 
     # ---- CPU baseline: the oracle on the host, bounded sample ---------------
     if args.cpu_seconds > 0:
@@ -391,6 +396,39 @@ def calibrate_copy(mib):
                       "launches": 8, "GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_ceiling(torch, stream, mib=1024, reps=6):
+    """A plain device-to-device copy of `mib` MiB (torch's copy_, which is
+    the HIP runtime's copy kernel), timed live, in GB/s of bytes read +
+    written: a reference for a kernel that moves as many bytes in as out."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        (b if i % 2 == 0 else a).copy_(a if i % 2 == 0 else b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(wl, st, budget_s, torch):
     import oracle
 
@@ -415,6 +453,7 @@ def cpu_baseline(wl, st, budget_s, torch):
     return {"value": round(bytes_done / t_used / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "ms_per_step": round(t_used * 1e3 / reps, 1),
+            "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count()},
             "sample": f"{reps} full step(s) of the {wl.name} layer (route+dispatch+combine+"
                       f"combine_bwd with dw), single-threaded C oracle, {t_used:.1f} s"}
 
