@@ -207,10 +207,19 @@ def test_route_random_tiny(seed):
     np.testing.assert_allclose(r.probs, exp, rtol=0, atol=0)
     # sync-free at the minimum capacity: same data rows, zero sentinel tail
     C = oracle.capacity_min(T, k, EL, P)
-    rs = oracle.route(idx, E, lb, EL, P, sync_free=True, C=C, w=w)
+    x = inputs.bf16_normal((T, 256), rng)
+    re_ = oracle.route(idx, E, lb, EL, P, w=w, x=x)
+    rs = oracle.route(idx, E, lb, EL, P, sync_free=True, C=C, w=w, x=x)
     check_route_against_library(idx, E, lb, EL, P, rs, sync_free=True, C=C, w=w)
     np.testing.assert_array_equal(rs.row_token[:r.total], r.row_token)
     np.testing.assert_array_equal(rs.row_of_slot, r.row_of_slot)
+    np.testing.assert_array_equal(rs.rows[:r.total], re_.rows)
+    data = re_.row_token >= 0
+    np.testing.assert_array_equal(re_.rows[data], x[re_.row_token[data]])
+    assert not re_.rows[~data].any()                   # pad rows: bf16 +0
+    assert not rs.rows[r.total:].any()                 # sentinel rows: bf16 +0
+    assert (rs.row_token[r.total:] == -1).all() and (rs.row_expert[r.total:] == EL).all()
+    assert not rs.row_w[r.total:].any()
 
 
 def test_top1_all_local_is_stable_argsort_and_combine_inverts():

@@ -38,6 +38,21 @@ MUTATIONS = [
     ("weight gradient of repeated ids dropped",
      "grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w) ? grad_row_w[r] : 0.0f;",
      "grad_topk_w[t * k + j] = (local && r >= 0 && r < R && grad_row_w && (j == 0 || idx[t * k + j - 1] != e)) ? grad_row_w[r] : 0.0f;"),
+    ("pad rows keep data", "row_w[r] = 0.0f;\n            if (rows)\n                memset(rows + r * H, 0,",
+     "row_w[r] = 0.0f;\n            if (rows)\n                memset(rows + r * H, 1,"),
+    ("sentinel rows keep data",
+     "memset(rows + r * H, 0, (size_t)H * sizeof(uint16_t));\n    }\n\n    free(W);",
+     "memset(rows + r * H, 1, (size_t)H * sizeof(uint16_t));\n    }\n\n    free(W);"),
+    ("sentinel rows left unwritten",
+     "memset(rows + r * H, 0, (size_t)H * sizeof(uint16_t));\n    }\n\n    free(W);",
+     "(void)0;\n    }\n\n    free(W);"),
+    ("combine leaves tokens without a local slot unwritten",
+     "for (int64_t h = 0; h < H; ++h) {\n            float s = have ? acc[h] : 0.0f;",
+     "for (int64_t h = 0; h < H * have; ++h) {\n            float s = have ? acc[h] : 0.0f;"),
+    ("local range starts one expert late", "if (e < 0 || e >= E || e < lb || e >= (int64_t)lb + EL)",
+     "if (e < 0 || e >= E || e <= lb || e >= (int64_t)lb + EL)"),
+    ("probs written as the plain multihot", "probs[i] = map[i] ? W[i] : 0.0f;",
+     "probs[i] = map[i] ? 1.0f : 0.0f;"),
 ]
 
 # FP8 dispatch, caught by tests/test_oracle_fp8.py
