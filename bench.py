@@ -101,7 +101,12 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 8 plain device-to-device copies of MIB MiB (torch copy_) and "
                          "exit: the reference kernel for scaling HBM traffic counters")
+    ap.add_argument("--cpu-worker", nargs=3, metavar=("DIR", "SECONDS", "WORKLOAD"),
+                    help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_worker:
+        cpu_worker(args.cpu_worker[0], float(args.cpu_worker[1]), args.cpu_worker[2])
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
@@ -429,33 +434,100 @@ def copy_ceiling(torch, stream, mib=1024, reps=6):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(wl, st, budget_s, torch):
+def oracle_steps(wl, a, budget_s, max_reps=500):
+    """Full steps of the single-threaded C oracle (route with the dispatched
+    rows, combine, combine backward with dw) on one layer's arrays, for about
+    budget_s seconds.  Returns (steps, seconds, algorithmic bytes)."""
     import oracle
 
-    idx, w = st["idx_np"], st["w_np"]
-    u16 = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
-    x, g = u16(st["x"]), u16(st["g"])
+    idx, w, x, g, Y, F = (a[n] for n in ("idx", "w", "x", "g", "Y", "F"))
     EL = wl.num_local
     C = wl.cap if wl.sync_free else 0
-    Y, F = u16(st["Y"]), u16(st["F"])
+    local = (idx >= wl.lb) & (idx < wl.lb + EL)
+    n_active = int(local.any(axis=1).sum())
     reps, t_used, bytes_done = 0, 0.0, 0
-    while t_used < budget_s and reps < 500:
+    while t_used < budget_s and reps < max_reps:
         t0 = time.perf_counter()
         r = oracle.route(idx, wl.E, wl.lb, EL, wl.P, sync_free=wl.sync_free, C=C, w=w, x=x,
                          want_probs=True)
         oracle.combine(idx, r.row_of_slot, Y[:r.R], wl.E, wl.lb, EL)
         oracle.combine_bwd(idx, r.row_of_slot, r.row_token, g, wl.E, wl.lb, EL, F=F[:r.R], R=r.R)
         t_used += time.perf_counter() - t0
-        local = (idx >= wl.lb) & (idx < wl.lb + EL)
-        bm = byte_model(wl, int(r.tpe.sum()), r.R, int(local.any(axis=1).sum()), 4, True)
+        bm = byte_model(wl, int(r.tpe.sum()), r.R, n_active, 4, True)
         bytes_done += sum(bm.values())
         reps += 1
-    return {"value": round(bytes_done / t_used / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "ms_per_step": round(t_used * 1e3 / reps, 1),
-            "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count()},
-            "sample": f"{reps} full step(s) of the {wl.name} layer (route+dispatch+combine+"
-                      f"combine_bwd with dw), single-threaded C oracle, {t_used:.1f} s"}
+    return reps, t_used, bytes_done
+
+
+def cpu_worker(arg_dir, budget_s, wname):
+    """One process of the all-cores leg: the arrays come memory-mapped from
+    arg_dir (no torch, no GPU); prints one JSON line."""
+    from combine_topk_idx_multihot_amd import inputs
+
+    a = {n: np.load(os.path.join(arg_dir, n + ".npy"), mmap_mode="r")
+         for n in ("idx", "w", "x", "g", "Y", "F")}
+    reps, t_used, bytes_done = oracle_steps(inputs.WORKLOADS[wname], a, budget_s)
+    print(json.dumps({"steps": reps, "seconds": t_used, "bytes": bytes_done}), flush=True)
+
+
+def host_cores():
+    """Cores this process may run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(wl, st, budget_s, torch):
+    """The oracle on the host, on a bounded sample of the same layer: one
+    thread in this process, then one unchanged single-threaded oracle per
+    host core in child processes (aggregate rate over their common wall
+    time)."""
+    import subprocess
+    import tempfile
+
+    u16 = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    a = {"idx": np.ascontiguousarray(st["idx_np"]), "w": np.ascontiguousarray(st["w_np"]),
+         "x": u16(st["x"]), "g": u16(st["g"]), "Y": u16(st["Y"]), "F": u16(st["F"])}
+    reps, t_used, bytes_done = oracle_steps(wl, a, budget_s)
+    out = {"value": round(bytes_done / t_used / 1e9, 3), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "ms_per_step": round(t_used * 1e3 / reps, 1),
+           "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count()},
+           "sample": f"{reps} full step(s) of the {wl.name} layer (route+dispatch+combine+"
+                     f"combine_bwd with dw), single-threaded C oracle, {t_used:.1f} s"}
+
+    n = host_cores()
+    budget_all = max(2.0, budget_s / 2)
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    with tempfile.TemporaryDirectory(prefix="moe_oracle_", dir=shm) as d:
+        for k, v in a.items():
+            np.save(os.path.join(d, k + ".npy"), v)
+        del a
+        wall0 = time.perf_counter()
+        procs = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", d,
+                                   str(budget_all), wl.name],
+                                  stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+                 for _ in range(n)]
+        res = []
+        for p in procs:
+            so, se = p.communicate(timeout=budget_all * 10 + 120)
+            if p.returncode != 0:
+                raise RuntimeError(f"oracle worker failed ({p.returncode}): {se[-500:]}")
+            res.append(json.loads(so.strip().splitlines()[-1]))
+        wall = time.perf_counter() - wall0
+    span = max(r["seconds"] for r in res)
+    steps = sum(r["steps"] for r in res)
+    out["all_cores"] = {
+        "value": round(sum(r["bytes"] for r in res) / span / 1e9, 3), "unit": "GB/s",
+        "cores": n, "processes": n,
+        "ms_per_step": round(span * 1e3 * n / steps, 1),
+        "sample": f"{n} processes, each the single-threaded C oracle on its own full steps of "
+                  f"the same layer (memory-mapped inputs): {steps} steps in {span:.1f} s of "
+                  f"oracle time ({wall:.1f} s wall with start-up); rate = all their bytes / the "
+                  f"longest process's oracle time"}
+    return out
 
 
 if __name__ == "__main__":

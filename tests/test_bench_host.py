@@ -84,3 +84,23 @@ def test_traffic_is_null_once_sources_change(monkeypatch):
         assert bench.measured_traffic(w, "combine_bwd") == int(t["workloads"][w]["combine_bwd"]["bytes"])
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
     assert bench.measured_traffic(w, "combine_bwd") is None
+
+
+def test_cpu_baseline_single_and_all_cores():
+    """The oracle leg on a tiny layer, with host tensors standing in for the
+    device buffers: one thread in-process, then one oracle per core in child
+    processes that read the same arrays memory-mapped."""
+    import torch
+
+    wl = inputs.WORKLOADS["tiny"]
+    idx, w = inputs.make_routing(wl, 1001)
+    R = wl.T * wl.k
+    gen = torch.Generator().manual_seed(5)
+    st = {"idx_np": idx, "w_np": w}
+    for n, rows in (("x", wl.T), ("g", wl.T), ("Y", R), ("F", R)):
+        st[n] = torch.randn((rows, wl.H), generator=gen).to(torch.bfloat16)
+    out = bench.cpu_baseline(wl, st, 0.3, torch)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    allc = out["all_cores"]
+    assert allc["cores"] == bench.host_cores() and allc["processes"] == allc["cores"]
+    assert allc["value"] > 0 and "processes" in allc["sample"]
