@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// block-wide scan helper (1024 threads)
+// wave scan helper
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 {
@@ -226,62 +226,54 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
     return v;
 }
 
-// Inclusive scan over a 1024-thread workgroup.  tmp: 16 ints of LDS.
-__device__ int block_incl_scan(int v, int *tmp)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    v = wave_incl_scan(v, lane);
-    if (lane == kWave - 1)
-        tmp[wave] = v;
-    __syncthreads();
-    if (wave == 0) {
-        int w = lane < 16 ? tmp[lane] : 0;
-        w = wave_incl_scan(w, lane);
-        if (lane < 16)
-            tmp[lane] = w;
-    }
-    __syncthreads();
-    if (wave > 0)
-        v += tmp[wave - 1];
-    __syncthreads();
-    return v;
-}
-
 // Publish tokens_per_expert, offsets and the status word from LDS totals.
-// Called by every thread of one 1024-thread workgroup.  With a host alias of
-// the status (eager mode, pinned host memory), the status is also written
-// there with system-scope stores, so the host needs no copy after the sync.
-__device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, int *tmp, int flags)
+// Called by every thread of one workgroup.  Wave 0 scans the padded totals
+// (lane l takes a run of consecutive experts, then a wave scan over the runs'
+// sums), and one barrier makes the offsets in LDS visible to the workgroup.
+// With a host alias of the status (eager mode, pinned host memory), the status
+// is also written there with system-scope stores, so the host needs no copy
+// after the sync.
+__device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, int flags)
 {
     __shared__ int32_t st[4];
     const int tid = threadIdx.x;
     const int EL = a.EL;
-    const int cnt = tid < EL ? tot[tid] : 0;
-    const int padded = tid < EL ? ((cnt + a.P - 1) / a.P) * a.P : 0;
-    const int incl = block_incl_scan(padded, tmp);
-    const int data_incl = block_incl_scan(cnt, tmp);
-    if (tid < EL)
-        offl[tid] = incl - padded;
-    if (tid == EL - 1)
-        offl[EL] = incl;
-    if (a.status) {
-        if (tid < EL) {
-            a.tpe[tid] = cnt;
-            a.off[tid] = incl - padded;
+    const int P = a.P;
+    if (tid < kWave) {
+        const int per = (EL + kWave - 1) / kWave;
+        const int e0 = min(EL, tid * per);
+        const int e1 = min(EL, e0 + per);
+        int sp = 0, sd = 0;
+        for (int e = e0; e < e1; ++e) {
+            const int c = tot[e];
+            sp += (c + P - 1) / P * P;
+            sd += c;
         }
-        if (tid == EL - 1) {
-            a.off[EL] = incl;
-            a.status[0] = incl;
-            a.status[2] = data_incl;
-            a.status[3] = 0;
-            st[0] = incl;
-            st[2] = data_incl;
-            st[3] = 0;
+        const int incl = wave_incl_scan(sp, tid);
+        const int data_incl = wave_incl_scan(sd, tid);
+        int run = incl - sp;
+        for (int e = e0; e < e1; ++e) {
+            const int c = tot[e];
+            offl[e] = run;
+            if (a.status) {
+                a.tpe[e] = c;
+                a.off[e] = run;
+            }
+            run += (c + P - 1) / P * P;
         }
-        if (tid == 0) {
-            a.status[1] = flags;
-            st[1] = flags;
+        if (tid == kWave - 1) {
+            offl[EL] = incl;
+            if (a.status) {
+                a.off[EL] = incl;
+                a.status[0] = incl;
+                a.status[1] = flags;
+                a.status[2] = data_incl;
+                a.status[3] = 0;
+                st[0] = incl;
+                st[1] = flags;
+                st[2] = data_incl;
+                st[3] = 0;
+            }
         }
     }
     __syncthreads();
@@ -304,7 +296,6 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     __shared__ int32_t pall[1024];  // [G][EL] partial totals
     __shared__ int32_t pbef[1024];  // [G][EL] partial sums over blocks before this one
     __shared__ int32_t offl[1025];  // offsets
-    __shared__ int32_t tmp[16];
     __shared__ int32_t flag_s;
     const int tid = threadIdx.x;
     const int EL = a.EL;
@@ -361,7 +352,7 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     RouteArgs pa = a;
     if (b != 0)
         pa.status = nullptr; // only block 0 publishes
-    publish(pa, pall, offl, tmp, flag_s);
+    publish(pa, pall, offl, flag_s);
 
     if (tid < nslots && packed >= 0) {
         const int ex = packed_expert(packed);
@@ -377,7 +368,6 @@ __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
     __shared__ int32_t part[1024]; // [G][EL] group sums, then group bases
     __shared__ int32_t tot[1024];
     __shared__ int32_t offl[1025];
-    __shared__ int32_t tmp[16];
     __shared__ int32_t flag_s;
     const int tid = threadIdx.x;
     const int EL = a.EL;
@@ -416,7 +406,7 @@ __global__ void __launch_bounds__(1024) k_route_scan(RouteArgs a)
         tot[tid] = run;
     }
     __syncthreads();
-    publish(a, tot, offl, tmp, flag_s);
+    publish(a, tot, offl, flag_s);
     if (g < G) {
         int run = part[g * EL + e];
         for (int64_t b = b0; b < b1; ++b) {
