@@ -295,8 +295,9 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
 {
     __shared__ int32_t pall[1024];  // [G][EL] partial totals
     __shared__ int32_t pbef[1024];  // [G][EL] partial sums over blocks before this one
+    __shared__ int32_t tot[1024];   // per-expert totals
+    __shared__ int32_t base[1024];  // this block's per-expert base
     __shared__ int32_t offl[1025];  // offsets
-    __shared__ int32_t flag_s;
     const int tid = threadIdx.x;
     const int EL = a.EL;
     const int64_t nblk = a.nblk;
@@ -308,15 +309,15 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     const int nslots = static_cast<int>((t1 - t0) * a.k);
     const int64_t s = t0 * a.k + tid;
     const int packed = tid < nslots ? a.row_of_slot[s] : -1;
-    if (tid == 0)
-        flag_s = 0;
-    __syncthreads();
-    if (b == 0) {
-        int f = 0;
-        for (int64_t bb = tid; bb < nblk; bb += 1024)
-            f |= a.blockflags[bb];
-        if (f)
-            atomicOr(&flag_s, f);
+    // block 0's first wave: the OR of every block's flags, in all its lanes
+    // (only that wave of that block publishes the status)
+    int flags = 0;
+    if (b == 0 && tid < kWave) {
+        for (int64_t bb = tid; bb < nblk; bb += kWave)
+            flags |= a.blockflags[bb];
+#pragma unroll
+        for (int o = kWave / 2; o >= 1; o >>= 1)
+            flags |= __shfl_xor(flags, o);
     }
     const int G = 1024 / EL;
     const int g = tid / EL;
@@ -336,27 +337,24 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
         pbef[g * EL + e] = before;
     }
     __syncthreads();
-    int tot_e = 0, base_e = 0;
     if (tid < EL) {
+        int tot_e = 0, base_e = 0;
         for (int gg = 0; gg < G; ++gg) {
             tot_e += pall[gg * EL + tid];
             base_e += pbef[gg * EL + tid];
         }
-    }
-    __syncthreads();
-    if (tid < EL) {
-        pall[tid] = tot_e;  // reuse: per-expert totals
-        pbef[tid] = base_e; // reuse: this block's per-expert base
+        tot[tid] = tot_e;
+        base[tid] = base_e;
     }
     __syncthreads();
     RouteArgs pa = a;
     if (b != 0)
         pa.status = nullptr; // only block 0 publishes
-    publish(pa, pall, offl, flag_s);
+    publish(pa, tot, offl, flags);
 
     if (tid < nslots && packed >= 0) {
         const int ex = packed_expert(packed);
-        a.row_of_slot[s] = offl[ex] + pbef[ex] + packed_rank(packed);
+        a.row_of_slot[s] = offl[ex] + base[ex] + packed_rank(packed);
     }
 }
 
