@@ -15,7 +15,8 @@ import torch
 
 from combine_topk_idx_multihot_amd import binding as B
 from combine_topk_idx_multihot_amd import inputs
-from test_gpu_parity import gpu, say  # noqa: F401 (gpu: fixture)
+import oracle
+from test_gpu_parity import gpu, say, to_dev_bf16, to_np_u16  # noqa: F401 (gpu: fixture)
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +123,44 @@ def test_route_dispatch_timed_and_repeated():
     ms = timer.elapsed_ms()
     say(f"[route_dispatch] timed call: {ms * 1e3:.1f} us (route and dispatch)")
     assert 0.0 < ms < 10.0
+
+
+EAGER_WORKLOADS = [n for n, wl in inputs.WORKLOADS.items() if not wl.sync_free]
+
+
+@pytest.mark.parametrize("name", EAGER_WORKLOADS)
+def test_route_dispatch_full_size_against_oracle(name):
+    """The call the benchmark times for eager layers, at the layer's full size
+    and into its worst-case buffers, held directly against the oracle."""
+    wl = inputs.WORKLOADS[name]
+    say(f"[route_dispatch] full size vs oracle: {name} T={wl.T} H={wl.H} E={wl.E} k={wl.k} "
+        f"P={wl.P}")
+    case = inputs.make_case(wl)
+    ref = oracle.route(case.idx, wl.E, wl.lb, wl.num_local, wl.P, w=case.w, x=case.x,
+                       want_probs=True)
+    assert ref.rc == oracle.OK
+    T, k, H = wl.T, wl.k, wl.H
+    d = B.make_desc(T, k, wl.E, wl.lb, wl.num_local, wl.P, B.MOE_EAGER, False, 0)
+    cap = B.moe_capacity_min(d)
+    h = B.alloc_handle(d)
+    idx_t = torch.from_numpy(np.ascontiguousarray(case.idx, np.int32)).cuda()
+    w_t = torch.from_numpy(np.ascontiguousarray(case.w, np.float32)).cuda()
+    probs = torch.empty((T, wl.E), dtype=torch.float32, device="cuda")
+    rows = torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")
+    row_w = torch.empty(cap, device="cuda")
+    rt = torch.empty(cap, dtype=torch.int32, device="cuda")
+    re = torch.empty(cap, dtype=torch.int32, device="cuda")
+    B.moe_route_dispatch(d, idx_t, h, to_dev_bf16(case.x), H, rows, w_t, probs, row_w, rt, re)
+    torch.cuda.synchronize()
+    R = h.total
+    assert R == ref.total and h.flags == ref.flags
+    np.testing.assert_array_equal(h.routing_map.cpu().numpy(), ref.map)
+    np.testing.assert_array_equal(h.tokens_per_expert.cpu().numpy(), ref.tpe)
+    np.testing.assert_array_equal(h.padded_offsets.cpu().numpy(), ref.off)
+    np.testing.assert_array_equal(h.row_of_slot.cpu().numpy(), ref.row_of_slot)
+    np.testing.assert_array_equal(probs.cpu().numpy().view(np.uint32), ref.probs.view(np.uint32))
+    np.testing.assert_array_equal(to_np_u16(rows[:R]), ref.rows)
+    np.testing.assert_array_equal(row_w[:R].cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+    np.testing.assert_array_equal(rt[:R].cpu().numpy(), ref.row_token)
+    np.testing.assert_array_equal(re[:R].cpu().numpy(), ref.row_expert)
+    say(f"  total={R} of {cap} rows, bit-exact")
