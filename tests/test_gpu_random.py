@@ -3,16 +3,20 @@ expert ranges, pad multiples, hidden sizes, both modes, both id widths,
 empty slots, repeated ids and out-of-range ids, drawn from one master seed.
 
 Every call of the path runs on each configuration (route, dispatch, combine,
-combine backward with dw, dispatch backward, FP8 dispatch) and is compared
-with the oracle exactly as in test_gpu_parity / test_gpu_fp8.
+combine backward with dw, dispatch backward, FP8 dispatch, and in eager mode
+the one-call route and dispatch) and is compared with the oracle exactly as in
+test_gpu_parity / test_gpu_fp8.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
+from combine_topk_idx_multihot_amd import binding as B
 from combine_topk_idx_multihot_amd import inputs
 from test_gpu_fp8 import RunFp8, check_all_rows, check_meta, check_sampled_rows
-from test_gpu_parity import Run, check_against_oracle, gpu, say  # noqa: F401 (gpu: fixture)
+from test_gpu_parity import (Run, check_against_oracle, gpu, say, to_dev_bf16,  # noqa: F401
+                             to_np_u16)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +71,41 @@ def test_random_configuration(i):
         check_all_rows(run8, ref8, x)
     else:
         check_sampled_rows(run8, ref8, x, n=32, seed=i)
+    if not sf:
+        check_route_dispatch(idx, w, x, E, lb, EL, P, c["idx64"], expect)
+
+
+def check_route_dispatch(idx, w, x, E, lb, EL, P, idx64, expect):
+    """moe_route_dispatch (the eager route and dispatch in one call, into
+    worst-case buffers) against the oracle: metadata, probs and rows [0, total)."""
+    T, k = idx.shape
+    H = x.shape[1]
+    ref = oracle.route(idx, E, lb, EL, P, w=w, x=x, want_probs=True)
+    d = B.make_desc(T, k, E, lb, EL, P, B.MOE_EAGER, idx64, 0)
+    cap = B.moe_capacity_min(d)
+    h = B.alloc_handle(d)
+    idx_t = torch.from_numpy(np.ascontiguousarray(idx, np.int64 if idx64 else np.int32)).cuda()
+    w_t = torch.from_numpy(np.ascontiguousarray(w, np.float32)).cuda()
+    probs = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    rows = torch.empty((cap, H), dtype=torch.bfloat16, device="cuda")
+    row_w = torch.empty(cap, device="cuda")
+    rt = torch.empty(cap, dtype=torch.int32, device="cuda")
+    re = torch.empty(cap, dtype=torch.int32, device="cuda")
+    rc = B.MOE_OK
+    try:
+        B.moe_route_dispatch(d, idx_t, h, to_dev_bf16(x), H, rows, w_t, probs, row_w, rt, re)
+    except B.MoeError as e:
+        rc = e.code
+    torch.cuda.synchronize()
+    assert rc == expect
+    R = h.total
+    assert R == ref.total and (h.flags & 3) == (ref.flags & 3)
+    np.testing.assert_array_equal(h.routing_map.cpu().numpy(), ref.map)
+    np.testing.assert_array_equal(h.tokens_per_expert.cpu().numpy(), ref.tpe)
+    np.testing.assert_array_equal(h.padded_offsets.cpu().numpy(), ref.off)
+    np.testing.assert_array_equal(h.row_of_slot.cpu().numpy(), ref.row_of_slot)
+    np.testing.assert_array_equal(probs.cpu().numpy().view(np.uint32), ref.probs.view(np.uint32))
+    np.testing.assert_array_equal(to_np_u16(rows[:R]), ref.rows)
+    np.testing.assert_array_equal(row_w[:R].cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
+    np.testing.assert_array_equal(rt[:R].cpu().numpy(), ref.row_token)
+    np.testing.assert_array_equal(re[:R].cpu().numpy(), ref.row_expert)
