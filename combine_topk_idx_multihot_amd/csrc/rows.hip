@@ -26,9 +26,10 @@
 //     their own interleaved with the copying ones, the dots of grad_out with
 //     the expert-output rows of the token's slots.  A token's row is dealt
 //     over 1 to 4 dot waves; each keeps its exact bf16 x bf16 products summed
-//     in fp64 registers, a butterfly ends each wave's part, and the token's
-//     first wave adds the parts in wave order through LDS before the single
-//     rounding to fp32, so dw is the same on every run.
+//     in fp64 registers, wave sums (one transposed butterfly for a batch of
+//     rows with 1 KiB segments, a butterfly per row otherwise) end each wave's
+//     part, and the token's first wave adds the parts in wave order through
+//     LDS before the single rounding to fp32, so dw is the same on every run.
 //   * pad rows are zeroed by extra workgroups of the rows' launch (one per
 //     expert).  The sync-free tail [total, R) -- most of the bytes when the
 //     worst case is far from the routed total -- is a launch of its own just
@@ -501,14 +502,45 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 // grad_out (move_token), and dw comes from dot workgroups of their own.  In a
 // dot workgroup a token's row is dealt over dot_wpt waves (1, 2 or 4), each
 // walking its segments of SEG chunks per lane with the fp64 partial dots of
-// up to kDotBatch rows in registers; a butterfly over each wave, then the
-// token's first wave adding its waves' sums in wave order through LDS, end
-// each batch.  So dw is the same on every run.  The dot workgroups hold only
+// up to kDotBatch rows in registers; the wave sums (wave_sums for 1 KiB
+// segments, a butterfly per row for larger ones), then the token's first wave
+// adding its waves' sums in wave order through LDS, end each batch.  So dw is the same on every run.  The dot workgroups hold only
 // dot waves, all running the same number of batch rounds, so their barriers
 // never wait on copying work.  Copy and dot workgroups are interleaved by
 // token: every four tokens get waves_per_token copy workgroups, then dot_wpt
 // dot workgroups.
 // ---------------------------------------------------------------------------
+// Wave sums of NB values per lane (NB a power of two, at most 64), in a fixed
+// order.  Each of the first log2(NB) exchange steps halves the values a lane
+// carries: the lane whose bit o is clear keeps the lower half of its values
+// and receives its partner's lower half, the other keeps and receives the
+// upper half, so both add the same two partial sums for each value they keep.
+// The remaining steps are a plain butterfly over the one value left.  At the
+// end v[0] of lane l holds the whole wave's sum of value (l >> (6 - log2 NB)),
+// the same in every lane of that group: 4 values take 8 exchanges instead of
+// the 24 of four separate butterflies.
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
+
+template <int NB>
+__device__ __forceinline__ void wave_sums(double (&v)[NB], int lane)
+{
+    static_assert(kWave == 64 && (NB & (NB - 1)) == 0 && NB <= kWave, "NB: a power of two <= 64");
+    int o = kWave / 2;
+#pragma unroll
+    for (int n = NB / 2; n >= 1; n >>= 1, o >>= 1) {
+        const bool upper = (lane & o) != 0;
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            const double keep = upper ? v[i + n] : v[i];
+            const double send = upper ? v[i] : v[i + n];
+            v[i] = keep + __shfl_xor(send, o);
+        }
+    }
+#pragma unroll
+    for (; o >= 1; o >>= 1)
+        v[0] += __shfl_xor(v[0], o);
+}
+
 template <int SEG>
 __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
 {
@@ -545,6 +577,18 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
                 for (int b = 0; b < kDotBatch; ++b)
                     if (b < bt.n)
                         load_seg<SEG, MOE_NT_DOT_F != 0>(f[b], a.F, bt.row[b], a.H, c0, nch, lane);
+                // 1 KiB segments: grad_out's 8 elements widened once for every
+                // row of the batch.  Larger segments widen them per use, which
+                // keeps 16 VGPRs per KiB free for occupancy.
+                constexpr bool kWiden = SEG == 1;
+                double gd[kWiden ? 8 : 1];
+                if constexpr (kWiden) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        gd[2 * q] = static_cast<double>(bf16_lo(v[0][q]));
+                        gd[2 * q + 1] = static_cast<double>(bf16_hi(v[0][q]));
+                    }
+                }
 #pragma unroll
                 for (int b = 0; b < kDotBatch; ++b) {
                     if (b < bt.n) {
@@ -554,10 +598,11 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
 #pragma unroll
                                 for (int q = 0; q < 4; ++q) {
                                     const uint32_t gw = v[i][q], fw = f[b][i][q];
-                                    part[b] = fma(static_cast<double>(bf16_lo(gw)),
-                                                  static_cast<double>(bf16_lo(fw)), part[b]);
-                                    part[b] = fma(static_cast<double>(bf16_hi(gw)),
-                                                  static_cast<double>(bf16_hi(fw)), part[b]);
+                                    const double g0 = kWiden ? gd[2 * q] : static_cast<double>(bf16_lo(gw));
+                                    const double g1 =
+                                        kWiden ? gd[2 * q + 1] : static_cast<double>(bf16_hi(gw));
+                                    part[b] = fma(g0, static_cast<double>(bf16_lo(fw)), part[b]);
+                                    part[b] = fma(g1, static_cast<double>(bf16_hi(fw)), part[b]);
                                 }
                             }
                         }
@@ -565,15 +610,26 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
                 }
             }
         }
+        if constexpr (SEG == 1) {
+            // all rows of the batch summed over the wave at once; row b ends
+            // in the lanes l with l >> kShift == b
+            constexpr int kShift = 6 - ilog2(kDotBatch);
+            wave_sums<kDotBatch>(part, lane);
+            const int b = lane >> kShift;
+            if ((lane & ((1 << kShift) - 1)) == 0 && b < bt.n)
+                red[wave][b] = part[0];
+        } else {
+            // one butterfly per row: fewer registers live at once
 #pragma unroll
-        for (int b = 0; b < kDotBatch; ++b) {
-            if (b < bt.n) {
-                double sum = part[b];
+            for (int b = 0; b < kDotBatch; ++b) {
+                if (b < bt.n) {
+                    double sum = part[b];
 #pragma unroll
-                for (int o = kWave / 2; o >= 1; o >>= 1)
-                    sum += __shfl_xor(sum, o);
-                if (lane == 0)
-                    red[wave][b] = sum;
+                    for (int o = kWave / 2; o >= 1; o >>= 1)
+                        sum += __shfl_xor(sum, o);
+                    if (lane == 0)
+                        red[wave][b] = sum;
+                }
             }
         }
         __syncthreads();
