@@ -98,6 +98,8 @@ def main():
                          "'' for none")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the FP8 dispatch and the dispatch backward")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-sized layers replayed from a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 8 plain device-to-device copies of MIB MiB (torch copy_) and "
                          "exit: the reference kernel for scaling HBM traffic counters")
@@ -143,6 +145,11 @@ def main():
             del s_
             result["also"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "config",
                                                       "us_per_layer", "roofline")}
+
+    # ---- decode-sized layers replayed from a captured HIP graph --------------
+    if not args.no_decode:
+        torch.cuda.empty_cache()
+        result["decode_graph"] = decode_graph(torch, B, inputs)
     print(json.dumps(result), flush=True)
 
 
@@ -410,6 +417,63 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+DECODE_SHAPES = ((1, 2048), (256, 2048), (1, 4096), (256, 4096))
+
+
+def decode_graph(torch, B, inputs, reps=200):
+    """Decode-sized layers: route + dispatch + combine in sync-free mode
+    (worst-case rows, nothing read back to the host), E = 128, top-8, on a
+    one-rank share of 32 experts (expert parallelism over 4 GPUs), captured
+    once in a HIP graph and replayed `reps` times back to back.  us per layer
+    from events around the replays, for T tokens of hidden size H.  The
+    captured work is the library's kernels only (no exchange, no experts)."""
+    E, k, EL, P = 128, 8, 32, 1
+    out = {"shape": {"E": E, "k": k, "local_experts": EL, "pad_multiple": P,
+                     "mode": "sync_free", "replays": reps}}
+    for T, H in DECODE_SHAPES:
+        rng = np.random.default_rng([77, T, H])
+        idx, w = inputs.topk_softmax(T, E, k, rng)
+        C = B.moe_capacity_min(B.make_desc(T, k, E, 0, EL, P, B.MOE_EAGER, False, 0))
+        d = B.make_desc(T, k, E, 0, EL, P, B.MOE_SYNC_FREE, False, C)
+        idx_t = torch.from_numpy(idx).cuda()
+        w_t = torch.from_numpy(w).cuda()
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(77 * T + H)
+        x = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+        h = B.alloc_handle(d)
+        rows = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
+        row_w = torch.empty(C, dtype=torch.float32, device="cuda")
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        s = torch.cuda.Stream()
+
+        def layer():
+            B.moe_route_build(d, idx_t, h, stream=s)
+            B.moe_dispatch(d, h, x, H, C, rows, w_t, row_w, stream=s)
+            B.moe_combine(d, h, rows, H, C, y, stream=s)
+
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            layer()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            g.capture_begin()
+            layer()
+            g.capture_end()
+            for _ in range(10):
+                g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        out[f"T{T}_H{H}_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        del g
+    return out
 
 
 def copy_ceiling(torch, stream, mib=1024, reps=6):
