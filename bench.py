@@ -25,7 +25,10 @@ implementation": distinct layers back to back):
     count is read back, so the device does not wait for the host between the
     two.  The per-kernel breakdown times the route and the dispatch as two
     calls (the same kernels on the same inputs); sync-free steps always use two
-    calls, with the dispatch through binding.PreparedDispatch.
+    calls, with the dispatch through binding.PreparedDispatch.  The combine
+    and its backward go through binding.PreparedCombine / PreparedCombineBwd
+    (buffers checked once, each step passes its row count), which keeps the
+    host's work between the eager readback and their launches small.
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
@@ -194,6 +197,11 @@ def measure(name, args, with_next, torch, B, inputs):
         st["dispatch"] = B.PreparedDispatch(d, st["h"], st["x"], H, st["rows"], st["w"],
                                             st["row_w"], st["row_token"], st["row_expert"],
                                             stream=stream)
+        # the combine and its backward, checked once likewise: after the eager
+        # readback the host has only the dispatch's run time to issue them
+        st["combine"] = B.PreparedCombine(d, st["h"], st["Y"], H, st["out"], stream=stream)
+        st["combine_bwd"] = B.PreparedCombineBwd(d, st["h"], st["g"], H, st["grad_rows"], st["F"],
+                                                 st["dw"], stream=stream)
         sets.append(st)
     torch.cuda.synchronize()
 
@@ -221,11 +229,10 @@ def measure(name, args, with_next, torch, B, inputs):
             R = st["h"].total
         if "combine" in t:
             t["combine"].arm()
-        B.moe_combine(d, st["h"], st["Y"], H, R, st["out"], stream=stream)
+        st["combine"](R)
         if "combine_bwd" in t:
             t["combine_bwd"].arm()
-        B.moe_combine_bwd(d, st["h"], st["g"], H, R, st["grad_rows"], st["F"], st["dw"],
-                          stream=stream)
+        st["combine_bwd"](R)
         return R
 
     for i in range(args.warmup):

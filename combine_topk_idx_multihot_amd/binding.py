@@ -7,7 +7,9 @@ tensor lives on the GPU, is contiguous, has the expected dtype and is large
 enough for what the call will write (the C ABI takes plain pointers and cannot).
 The convenience functions at the bottom (``alloc_handle``, ``route``,
 ``dispatch``, ``dispatch_fp8``, ``combine``, ``combine_bwd``, ``dispatch_bwd``)
-only add output allocation.
+only add output allocation.  ``PreparedDispatch``, ``PreparedCombine`` and
+``PreparedCombineBwd`` check reused buffers once and then take only the step's
+row count; ``KernelTimer`` times one call's kernels.
 
 The library is loaded on first use; if it has not been built this raises
 (there is no fallback path).
@@ -346,6 +348,73 @@ class PreparedDispatch:
             raise MoeError(MOE_ERR_ARG, f"R={R} outside [0, {self.capacity}] rows of the buffers")
         return _check(self._fn(*self._head, R, *self._tail))
 
+
+
+class PreparedCombine:
+    """moe_combine over buffers that a loop reuses on every step, checked once.
+
+    Y holds up to `capacity` rows of H (for instance the experts' output
+    buffer sized for the worst case); each call passes only the step's row
+    count R and combines rows [0, R) into `out`.  As with PreparedDispatch,
+    the Python-side checks are made here once, which takes them off the path
+    between the eager readback and the launch; the library still checks every
+    argument on every call.  The tensors must stay as they are while the
+    object is in use; it holds references to them.
+    """
+
+    def __init__(self, desc: Desc, handle: Handle, Y: torch.Tensor, H: int, out: torch.Tensor,
+                 stream=None):
+        if H <= 0 or Y is None:
+            raise MoeError(MOE_ERR_ARG, "H must be positive and Y given")
+        cap = Y.numel() // H
+        p_y = _dev(Y, "Y", _BF16, cap * H) if cap else None
+        p_o = _dev(out, "out", (torch.bfloat16, torch.float32), desc.T * H) if desc.T else None
+        self.capacity = cap
+        self._fn = lib().moe_combine
+        self._desc = Desc.from_buffer_copy(desc)
+        self._head = (ctypes.byref(self._desc), handle.cref(), p_y, H)
+        self._tail = (p_o, int(out.dtype == torch.float32), _stream(stream))
+        self._keep = (handle, Y, out)
+
+    def __call__(self, R: int) -> int:
+        if not 0 <= R <= self.capacity:
+            raise MoeError(MOE_ERR_ARG, f"R={R} outside [0, {self.capacity}] rows of the buffers")
+        return _check(self._fn(*self._head, R, *self._tail))
+
+
+class PreparedCombineBwd:
+    """moe_combine_bwd over buffers that a loop reuses on every step, checked
+    once: grad_rows (and expert_out, when dw is wanted) hold up to `capacity`
+    rows; each call passes only the step's row count R.  Same contract as
+    PreparedCombine."""
+
+    def __init__(self, desc: Desc, handle: Handle, grad_out: torch.Tensor, H: int,
+                 grad_rows: torch.Tensor, expert_out: torch.Tensor | None = None,
+                 dw: torch.Tensor | None = None, stream=None):
+        if H <= 0 or grad_rows is None:
+            raise MoeError(MOE_ERR_ARG, "H must be positive and grad_rows given")
+        if (expert_out is None) != (dw is None):
+            raise MoeError(MOE_ERR_ARG, "expert_out and dw go together")
+        cap = grad_rows.numel() // H
+        if expert_out is not None:
+            cap = min(cap, expert_out.numel() // H)
+        p_g = _dev(grad_out, "grad_out", _BF16, desc.T * H) if desc.T else None
+        p_gr = _dev(grad_rows, "grad_rows", _BF16, cap * H) if cap else None
+        p_f = _dev(expert_out, "expert_out", _BF16, cap * H, optional=True) if cap else None
+        p_dw = _dev(dw, "dw", _F32, desc.T * desc.k, optional=True) if p_f is not None else None
+        if desc.T == 0:  # no slot: nothing for dw to hold, expert_out is not read
+            p_f = p_dw = None
+        self.capacity = cap
+        self._fn = lib().moe_combine_bwd
+        self._desc = Desc.from_buffer_copy(desc)
+        self._head = (ctypes.byref(self._desc), handle.cref(), p_g, p_f, H)
+        self._tail = (p_gr, p_dw, _stream(stream))
+        self._keep = (handle, grad_out, grad_rows, expert_out, dw)
+
+    def __call__(self, R: int) -> int:
+        if not 0 <= R <= self.capacity:
+            raise MoeError(MOE_ERR_ARG, f"R={R} outside [0, {self.capacity}] rows of the buffers")
+        return _check(self._fn(*self._head, R, *self._tail))
 
 def moe_dispatch_fp8(desc: Desc, handle: Handle, x: torch.Tensor, H: int, R: int,
                      rows_q: torch.Tensor, row_scale: torch.Tensor,
