@@ -26,9 +26,9 @@
 //     their own interleaved with the copying ones, the dots of grad_out with
 //     the expert-output rows of the token's slots.  A token's row is dealt
 //     over 1 to 4 dot waves; each keeps its exact bf16 x bf16 products summed
-//     in fp64 registers, wave sums (one transposed butterfly for a batch of
-//     rows with 1 KiB segments, a butterfly per row otherwise) end each wave's
-//     part, and the token's first wave adds the parts in wave order through
+//     in fp64 registers, wave sums (for a batch of four rows with 1 KiB
+//     segments, lane-half swaps and DPP moves without LDS; a butterfly per
+//     row otherwise) end each wave's part, and the token's first wave adds the parts in wave order through
 //     LDS before the single rounding to fp32, so dw is the same on every run.
 //   * pad rows are zeroed by extra workgroups of the rows' launch (one per
 //     expert).  The sync-free tail [total, R) -- most of the bytes when the
@@ -502,43 +502,81 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 // grad_out (move_token), and dw comes from dot workgroups of their own.  In a
 // dot workgroup a token's row is dealt over dot_wpt waves (1, 2 or 4), each
 // walking its segments of SEG chunks per lane with the fp64 partial dots of
-// up to kDotBatch rows in registers; the wave sums (wave_sums for 1 KiB
-// segments, a butterfly per row for larger ones), then the token's first wave
-// adding its waves' sums in wave order through LDS, end each batch.  So dw is the same on every run.  The dot workgroups hold only
+// up to kDotBatch rows in registers; the wave sums (wave_sums4 for 1 KiB
+// segments and batches of four, a butterfly per row otherwise), then the
+// token's first wave adding its waves' sums in wave order through LDS, end
+// each batch.  So dw is the same on every run.  The dot workgroups hold only
 // dot waves, all running the same number of batch rounds, so their barriers
 // never wait on copying work.  Copy and dot workgroups are interleaved by
 // token: every four tokens get waves_per_token copy workgroups, then dot_wpt
 // dot workgroups.
 // ---------------------------------------------------------------------------
-// Wave sums of NB values per lane (NB a power of two, at most 64), in a fixed
-// order.  Each of the first log2(NB) exchange steps halves the values a lane
-// carries: the lane whose bit o is clear keeps the lower half of its values
-// and receives its partner's lower half, the other keeps and receives the
-// upper half, so both add the same two partial sums for each value they keep.
-// The remaining steps are a plain butterfly over the one value left.  At the
-// end v[0] of lane l holds the whole wave's sum of value (l >> (6 - log2 NB)),
-// the same in every lane of that group: 4 values take 8 exchanges instead of
-// the 24 of four separate butterflies.
-constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
-
-template <int NB>
-__device__ __forceinline__ void wave_sums(double (&v)[NB], int lane)
+// Exchange of two fp64 values across lane halves with gfx950's lane-half
+// swaps: v_permlane32_swap (O = 32) trades the upper 32 lanes of its first
+// operand with the lower 32 lanes of its second, v_permlane16_swap (O = 16)
+// the odd 16-lane rows of the first with the even rows of the second.  After
+// swapping (a, b), a lane whose bit O is clear holds (its a, its partner's a)
+// and the other lane (its partner's b, its b), so one add leaves each lane
+// the two-lane sum of the value it keeps: a in the lower lanes, b in the
+// upper ones.
+template <int O>
+__device__ __forceinline__ double swap_halves_add(double a, double b)
 {
-    static_assert(kWave == 64 && (NB & (NB - 1)) == 0 && NB <= kWave, "NB: a power of two <= 64");
-    int o = kWave / 2;
-#pragma unroll
-    for (int n = NB / 2; n >= 1; n >>= 1, o >>= 1) {
-        const bool upper = (lane & o) != 0;
-#pragma unroll
-        for (int i = 0; i < n; ++i) {
-            const double keep = upper ? v[i + n] : v[i];
-            const double send = upper ? v[i] : v[i + n];
-            v[i] = keep + __shfl_xor(send, o);
-        }
+    static_assert(O == 16 || O == 32, "lane-half swaps exist for 16 and 32");
+    const uint64_t ua = static_cast<uint64_t>(__double_as_longlong(a));
+    const uint64_t ub = static_cast<uint64_t>(__double_as_longlong(b));
+    const uint32_t alo = static_cast<uint32_t>(ua), ahi = static_cast<uint32_t>(ua >> 32);
+    const uint32_t blo = static_cast<uint32_t>(ub), bhi = static_cast<uint32_t>(ub >> 32);
+    uint32_t na_lo, na_hi, nb_lo, nb_hi;
+    if constexpr (O == 32) {
+        const auto lo = __builtin_amdgcn_permlane32_swap(alo, blo, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(ahi, bhi, false, false);
+        na_lo = lo[0], nb_lo = lo[1], na_hi = hi[0], nb_hi = hi[1];
+    } else {
+        const auto lo = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+        na_lo = lo[0], nb_lo = lo[1], na_hi = hi[0], nb_hi = hi[1];
     }
-#pragma unroll
-    for (; o >= 1; o >>= 1)
-        v[0] += __shfl_xor(v[0], o);
+    const double na = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(na_hi) << 32) | na_lo));
+    const double nb = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(nb_hi) << 32) | nb_lo));
+    return na + nb;
+}
+
+// An fp64 value moved across lanes by a DPP lane pattern (within each 16-lane
+// row; every source lane exists for the patterns used here).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false));
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i in each 8-lane half-row
+constexpr int kDppMirror = 0x140;    // lane i <-> 15 - i in each 16-lane row
+
+// Wave sums of the 4 fp64 values each lane holds (one per row of a dot
+// batch), in a fixed order and without LDS.  Two lane-half exchanges halve
+// the values a lane carries (4 -> 2 -> 1; lane l keeps row 2*bit5 + bit4 of
+// l, i.e. l >> 4); then each 16-lane row is summed by DPP: xor 1 and xor 2,
+// then the half-row and row mirrors, which pair the already equal quads and
+// half-rows as xor 4 and xor 8 would.  Every lane of row group b ends with
+// the wave's sum of value b.
+__device__ __forceinline__ double wave_sums4(double (&v)[4])
+{
+    v[0] = swap_halves_add<32>(v[0], v[2]);
+    v[1] = swap_halves_add<32>(v[1], v[3]);
+    double s = swap_halves_add<16>(v[0], v[1]);
+    s = s + dpp_f64<kDppXor1>(s);
+    s = s + dpp_f64<kDppXor2>(s);
+    s = s + dpp_f64<kDppHalfMirror>(s);
+    s = s + dpp_f64<kDppMirror>(s);
+    return s;
 }
 
 template <int SEG>
@@ -610,14 +648,13 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
                 }
             }
         }
-        if constexpr (SEG == 1) {
-            // all rows of the batch summed over the wave at once; row b ends
-            // in the lanes l with l >> kShift == b
-            constexpr int kShift = 6 - ilog2(kDotBatch);
-            wave_sums<kDotBatch>(part, lane);
-            const int b = lane >> kShift;
-            if ((lane & ((1 << kShift) - 1)) == 0 && b < bt.n)
-                red[wave][b] = part[0];
+        if constexpr (SEG == 1 && kDotBatch == 4) {
+            // the batch's four rows summed over the wave at once; row b ends
+            // in lanes 16 b .. 16 b + 15
+            const double sum = wave_sums4(part);
+            const int b = lane >> 4;
+            if ((lane & 15) == 0 && b < bt.n)
+                red[wave][b] = sum;
         } else {
             // one butterfly per row: fewer registers live at once
 #pragma unroll
