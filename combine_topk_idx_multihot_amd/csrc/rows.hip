@@ -28,8 +28,9 @@
 //     over 1 to 4 dot waves; each keeps its exact bf16 x bf16 products summed
 //     in fp64 registers, wave sums (for a batch of four rows with 1 KiB
 //     segments, lane-half swaps and DPP moves without LDS; a butterfly per
-//     row otherwise) end each wave's part, and the token's first wave adds the parts in wave order through
-//     LDS before the single rounding to fp32, so dw is the same on every run.
+//     row otherwise) end each wave's part, and the token's first wave adds
+//     the parts in wave order through LDS before the single rounding to fp32,
+//     so dw is the same on every run.
 //   * pad rows are zeroed by extra workgroups of the rows' launch (one per
 //     expert).  The sync-free tail [total, R) -- most of the bytes when the
 //     worst case is far from the routed total -- is a launch of its own just
@@ -37,7 +38,9 @@
 //     order: the writes in flight then form one window sliding through the
 //     tail, which MI355X's HBM takes markedly faster than the same writes
 //     spread over the range.  In eager mode the tail is normally empty; a few
-//     workgroups of the rows' launch cover it in 64 KiB wave tasks.
+//     workgroups of the rows' launch cover it in 64 KiB wave tasks.  A
+//     sync-free worst case of at most 32 MiB of rows (decode sizes) is zeroed
+//     the same way, by workgroups of the rows' launch, saving a launch.
 //   * combine adds the token's rows in fp32 in ascending slot order (the
 //     accumulator starts from the first row) and writes bf16 (nearest-even)
 //     or fp32; one wave per (token, segment).
@@ -455,9 +458,11 @@ __device__ __forceinline__ void fill_sentinel_oneshot(const RowArgs &a, int64_t 
     }
 }
 
-// Rows [total, R) in eager mode (normally none: R is the total read back;
-// a different R sets flag bit 2): zero data, token -1, expert EL (the
-// sentinel), weight 0, by a few workgroups of the rows' launch.
+// Rows [total, R) by workgroups of the rows' launch: in eager mode (normally
+// none: R is the total read back; a different R sets flag bit 2), and in
+// sync-free mode when the worst-case row array is small
+// (tail_in_rows_launch): zero data, token -1, expert EL (the sentinel),
+// weight 0.
 __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
 {
     const int64_t total = a.status[0];
@@ -480,8 +485,9 @@ __device__ __forceinline__ void fill_sentinel(const RowArgs &a, int64_t sb)
 }
 
 // Grid: [sentinel blocks][token blocks][expert blocks].  Sentinel blocks are
-// eager mode's few workgroups for the (normally empty) [total, R); in
-// sync-free mode the tail has a launch of its own and there are none here.
+// eager mode's few workgroups for the (normally empty) [total, R), or the
+// workgroups that zero a small sync-free tail; a large sync-free tail has a
+// launch of its own and there are none here.
 template <int SEG>
 __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 {
@@ -969,9 +975,28 @@ static int chunks_per_lane(int H)
     return n;
 }
 
+// A sync-free worst-case row array of at most this many bytes has its tail
+// zeroed by workgroups of the rows' launch, in 64 KiB wave tasks as in eager
+// mode, instead of by a launch of its own: at decode sizes a second launch
+// costs more than the writes.  Larger arrays keep the one-shot tail launch,
+// whose address-ordered writes are the faster way to zero hundreds of MB.
+constexpr int64_t kInlineTailBytes = int64_t(32) << 20;
+
+static int64_t row_array_bytes(const RowArgs &a)
+{
+    return a.rows_q ? a.R * (a.H + (a.H >> 7) * 4) : a.R * 2 * a.H;
+}
+
+static bool tail_in_rows_launch(const RowArgs &a)
+{
+    return !a.eager && !a.keep_tail && row_array_bytes(a) <= kInlineTailBytes;
+}
+
 // Sentinel-fill workgroups: in sync-free mode, those of the tail's own
-// launch, one piece per wave over the whole worst-case row array; eager mode
-// keeps a handful in the rows' launch for the (normally empty) [total, R).
+// launch, one piece per wave over the whole worst-case row array, or for a
+// small array enough of the rows' launch for one 64 KiB task per wave; eager
+// mode keeps a handful in the rows' launch for the (normally empty)
+// [total, R).
 static int64_t sentinel_blocks(const RowArgs &a)
 {
     // always a multiple of 8, so that the workgroups after them keep their
@@ -980,6 +1005,11 @@ static int64_t sentinel_blocks(const RowArgs &a)
         return 0;
     if (a.eager)
         return 8;
+    if (tail_in_rows_launch(a)) {
+        const int64_t task_bytes = kZeroTask * 16;
+        const int64_t tasks = (row_array_bytes(a) + task_bytes - 1) / task_bytes;
+        return ((tasks + kRowWaves - 1) / kRowWaves + 7) / 8 * 8;
+    }
     // sync-free: the tail's own launch, one piece per wave over the whole row
     // array (the host does not know where the tail starts), and over the
     // scale array of E4M3 rows
@@ -1038,7 +1068,7 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
     RowArgs a = a0;
     if (!move_rows_fits(a0))
         return hipErrorInvalidConfiguration;
-    if (!a0.eager && a0.nsent_blocks > 0) {
+    if (!a0.eager && a0.nsent_blocks > 0 && !tail_in_rows_launch(a0)) {
         // sync-free: the tail first, on its own, then the rows
         launch(k_sentinel_oneshot, dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s, a0);
         a.nsent_blocks = 0;
