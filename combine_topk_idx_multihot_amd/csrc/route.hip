@@ -25,6 +25,9 @@
 //                    global totals, scans the padded totals into offsets in LDS
 //                    and rewrites its slots to final rows; block 0 publishes
 //                    tokens_per_expert, offsets and the status word.
+//   A route that fits one K1 workgroup (decode sizes) ends in K1: its block
+//   counts are the totals, so it publishes offsets and status and writes the
+//   final rows itself, and K2 is not launched.
 //   Large T (count table > 64 Ki entries) takes a three-launch form instead:
 //   K2s route_scan (one workgroup) then K3 route_rows (one thread per slot).
 #include "moe_internal.h"
@@ -71,8 +74,11 @@ static size_t count_lds_bytes(int threads, int EL)
 {
     const size_t words = static_cast<size_t>(EL) * (threads / 32);
     return words * 4 + ((words + 1) & ~static_cast<size_t>(1)) * 2 +
-           static_cast<size_t>(threads) * 8 + 4;
+           static_cast<size_t>(threads) * 8 + 4 +
+           (2 * static_cast<size_t>(EL) + 1) * 4; // totals and offsets (one-block routes)
 }
+
+__device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, int flags);
 
 template <typename IT>
 __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
@@ -86,6 +92,8 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
     int32_t *sid = reinterpret_cast<int32_t *>(pref + ((EL * W + 1) & ~1)); // staged ids
     float *sw = reinterpret_cast<float *>(sid + nthreads);                   // staged weights
     int32_t *bflag = reinterpret_cast<int32_t *>(sw + nthreads);
+    int32_t *tot = bflag + 1;  // [EL] the block's counts (one-block routes)
+    int32_t *offl = tot + EL;  // [EL+1] offsets (one-block routes)
 
     const IT *__restrict__ idx = static_cast<const IT *>(a.idx);
     const int tid = threadIdx.x;
@@ -191,12 +199,31 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
             }
         }
         pref[i] = static_cast<uint16_t>(incl - c);
-        if ((i & (W - 1)) == W - 1)
+        if ((i & (W - 1)) == W - 1) {
             a.counts[b * EL + i / W] = incl;
+            tot[i / W] = incl;
+        }
     }
     if (tid == 0)
         a.blockflags[b] = bf;
     __syncthreads();
+
+    if (a.nblk == 1) {
+        // The whole route is this workgroup: its counts are the totals, so it
+        // publishes the offsets and the status itself and writes final rows;
+        // no finishing pass is launched.
+        publish(a, tot, offl, bf);
+        if (tid < nslots) {
+            int v = -1;
+            if (ep >= 0) {
+                const int p = tid - prim_back;
+                const int w = p >> 5;
+                v = offl[ep] + pref[ep * W + w] + __popc(bm[ep * W + w] & ((1u << (p & 31)) - 1u));
+            }
+            a.row_of_slot[s] = v;
+        }
+        return;
+    }
 
     // In-block rank = earlier slots of the same expert = prefix + popcount of
     // the bits below the owning slot (the first slot, for a repeated id).
@@ -440,6 +467,8 @@ hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }
+    if (a.nblk == 1)
+        return hipSuccess; // the counting pass finished the route (one workgroup)
     if (a.nblk > 0 && a.nblk * a.EL <= kFusedFinishMax) {
         launch(k_route_finish, dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s, a);
         return hipGetLastError();
