@@ -231,6 +231,13 @@ EDGE = [
     ("max_local_sync_free", 300, 1500, 6, 400, 1024, 2, True, 512, 0.05, False, False),
     ("max_k_64", 200, 100, 64, 10, 80, 2, False, 256, 0.05, False, False),
     ("max_k_64_sync_free", 100, 64, 64, 0, 64, 1, True, 256, 0.0, False, False),
+    # the route in one counting workgroup (512 slots at k = 8; 256 with more
+    # than 512 local experts) and one token past it
+    ("one_route_block", 64, 128, 8, 0, 128, 16, False, 512, 0.05, False, False),
+    ("two_route_blocks", 65, 128, 8, 0, 128, 16, False, 512, 0.05, False, False),
+    ("one_route_block_sync_free", 64, 128, 8, 0, 32, 1, True, 512, 0.0, False, False),
+    ("one_route_block_1024_local", 32, 1024, 8, 0, 1024, 2, True, 256, 0.05, True, False),
+    ("two_route_blocks_1024_local", 33, 1024, 8, 0, 1024, 2, False, 256, 0.05, False, True),
 ]
 
 
