@@ -238,6 +238,10 @@ EDGE = [
     ("one_route_block_sync_free", 64, 128, 8, 0, 32, 1, True, 512, 0.0, False, False),
     ("one_route_block_1024_local", 32, 1024, 8, 0, 1024, 2, True, 256, 0.05, True, False),
     ("two_route_blocks_1024_local", 33, 1024, 8, 0, 1024, 2, False, 256, 0.05, False, True),
+    # sync-free row arrays on both sides of 32 MiB: the tail zeroed by the
+    # rows' launch (16381 rows of 2 KiB) or by a launch of its own (16389)
+    ("tail_in_rows_launch", 2047, 128, 8, 0, 16, 1, True, 1024, 0.0, False, False),
+    ("tail_launch_of_its_own", 2048, 128, 8, 0, 16, 1, True, 1024, 0.0, False, False),
 ]
 
 
