@@ -662,7 +662,9 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
             if ((lane & 15) == 0 && b < bt.n)
                 red[wave][b] = sum;
         } else {
-            // one butterfly per row: fewer registers live at once
+            // one butterfly per row: fewer registers live at once.  Every
+            // lane ends with the row's wave sum, so a wave that is its
+            // token's only dot wave takes its dots from there, with no LDS.
 #pragma unroll
             for (int b = 0; b < kDotBatch; ++b) {
                 if (b < bt.n) {
@@ -670,10 +672,18 @@ __device__ __forceinline__ void dot_tokens(const RowArgs &a, int64_t db)
 #pragma unroll
                     for (int o = kWave / 2; o >= 1; o >>= 1)
                         sum += __shfl_xor(sum, o);
-                    if (lane == 0)
+                    if (wpt == 1) {
+                        if (sl.valid && sl.first == bt.lane[b])
+                            mydw = static_cast<float>(sum);
+                    } else if (lane == 0) {
                         red[wave][b] = sum;
+                    }
                 }
             }
+            // one dot wave per token (the same for the whole workgroup): no
+            // exchange between waves, so no barrier
+            if (wpt == 1)
+                continue;
         }
         __syncthreads();
         if (wt == 0) {
