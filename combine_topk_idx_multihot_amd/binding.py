@@ -555,8 +555,10 @@ class KernelTimer:
             if e:
                 self._L.hipEventDestroy(e)
 
-    def __del__(self):
-        if sys.is_finalizing():  # the HIP runtime may already be torn down
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # bound at definition: at interpreter exit this module's globals (sys
+        # among them) may already be gone, and the HIP runtime torn down
+        if _finalizing():
             return
         try:
             self.close()

@@ -276,3 +276,11 @@ def test_route_dispatch_argument_rules():
     assert rd_rc(d, probs=FAKE) == B.MOE_ERR_ARG        # probs without topk_w
     assert rd_rc(d, w=FAKE) == B.MOE_ERR_ARG            # weights with nothing to write
     assert rd_rc(_desc(k=0)) == B.MOE_ERR_ARG
+
+
+def test_kernel_timer_destructor_at_interpreter_exit(monkeypatch):
+    """At interpreter exit a module's globals may already be cleared when a
+    KernelTimer is collected; its destructor must not raise then."""
+    t = B.KernelTimer.__new__(B.KernelTimer)  # no events: nothing to destroy
+    monkeypatch.setattr(B, "sys", None)
+    t.__del__()
