@@ -20,8 +20,8 @@
 //     per wave), and a token's segments are dealt over 1, 2 or 4 waves of the
 //     workgroup, so that even a few thousand tokens keep enough waves (and
 //     bytes) in flight on 256 CUs.  Within a segment a wave issues the loads
-//     of a batch of rows (8 for combine, 4 for the dots) before consuming any
-//     of them.
+//     of a batch of rows (4 for combine and for the dots) before consuming
+//     any of them.
 //   * the combine backward is the dispatch of grad_out plus, in workgroups of
 //     their own interleaved with the copying ones, the dots of grad_out with
 //     the expert-output rows of the token's slots.  A token's row is dealt
@@ -104,7 +104,7 @@
 #define MOE_DOT_BATCH 4
 #endif
 #ifndef MOE_COMBINE_BATCH
-#define MOE_COMBINE_BATCH 8
+#define MOE_COMBINE_BATCH 4
 #endif
 
 
