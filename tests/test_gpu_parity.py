@@ -242,6 +242,19 @@ EDGE = [
     # rows' launch (16381 rows of 2 KiB) or by a launch of its own (16389)
     ("tail_in_rows_launch", 2047, 128, 8, 0, 16, 1, True, 1024, 0.0, False, False),
     ("tail_launch_of_its_own", 2048, 128, 8, 0, 16, 1, True, 1024, 0.0, False, False),
+    # the route's three-launch form, taken when the count table (route blocks
+    # x local experts) passes 65536 entries: 66 blocks x 1024 local experts;
+    # 512 blocks x 128 (65536, the last fused-finish size) against 513 and
+    # 516 blocks x 128; eager, sync-free, repeated and bad ids
+    ("large_route_1024_local", 2100, 1024, 8, 0, 1024, 2, False, 256, 0.05, False, False),
+    ("large_route_1024_local_sync_free", 2100, 1024, 8, 0, 1024, 2, True, 256, 0.05, False,
+     False),
+    ("fused_finish_at_limit", 32768, 128, 8, 0, 128, 16, False, 256, 0.02, False, False),
+    ("large_route_past_limit", 32769, 128, 8, 0, 128, 16, False, 256, 0.02, False, False),
+    ("large_route_128_local", 33000, 128, 8, 0, 128, 16, False, 256, 0.02, False, False),
+    ("large_route_128_local_sync_free", 33000, 128, 8, 0, 128, 1, True, 256, 0.0, False, False),
+    ("large_route_share_sync_free", 33000, 128, 8, 16, 16, 4, True, 256, 0.02, True, False),
+    ("large_route_dups_bad_ids", 33000, 128, 8, 0, 128, 4, False, 256, 0.05, True, True),
 ]
 
 

@@ -28,6 +28,8 @@ CASES = [
     ("bad_ids", 500, 16, 4, 0, 16, 2, 256, 0.1, 0.05, True),
     ("one_token", 1, 8, 4, 2, 5, 4, 256, 0.0, 0.0, True),
     ("no_tokens", 0, 8, 2, 0, 8, 4, 256, 0.0, 0.0, True),
+    # the route's three-launch form (516 route blocks x 128 local experts)
+    ("large_route", 33000, 128, 8, 0, 128, 16, 256, 0.02, 0.0, True),
 ]
 
 
