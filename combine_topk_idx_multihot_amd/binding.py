@@ -151,10 +151,17 @@ _U8, _I32, _I64, _F32, _BF16 = ((torch.uint8,), (torch.int32,), (torch.int64,), 
                                 (torch.bfloat16,))
 
 
+# torch's raw current-stream query skips building a Stream object (a few
+# microseconds per call); it is not public API, so the public query stands in
+# where a torch build lacks it.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int:
     if stream is None:
-        # the current stream of the current device, without building a Stream object
-        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+        if _raw_current_stream is not None:
+            return _raw_current_stream(torch.cuda.current_device())
+        return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)

@@ -11,12 +11,23 @@
 #include "moe_mi355x.h"
 #include "moe_internal.h"
 
-#include <immintrin.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <chrono>
+#include <thread>
+
+// The host's wait for the eager row count spins on a word of pinned memory;
+// the spin hint is the x86 pause where there is one, a yield elsewhere.
+static inline void spin_hint()
+{
+#if defined(__x86_64__) || defined(__i386__)
+    __builtin_ia32_pause();
+#else
+    std::this_thread::yield();
+#endif
+}
 
 namespace {
 
@@ -326,7 +337,7 @@ int route_wait(const moe_handle *handle, int32_t *host_status, void *stream,
     if (a.host_status) {
         const auto t0 = std::chrono::steady_clock::now();
         while (!(ready = (hs[3] == 0))) {
-            _mm_pause();
+            spin_hint();
             if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(5))
                 break;
         }

@@ -17,9 +17,11 @@
  *
  * Conventions for every entry point
  *   - All tensors are caller-allocated; the library never allocates device
- *     memory and keeps no state between calls.  "device" pointers are HIP
- *     device (or managed) memory on the current device; "host" pointers are
- *     host memory.
+ *     memory.  "device" pointers are HIP device (or managed) memory on the
+ *     current device; "host" pointers are host memory.
+ *   - State kept between calls, per host thread: the message of
+ *     moe_last_error() and a pending moe_time_next_call() request (consumed
+ *     by the next call).  Nothing else outlives a call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch goes on that stream.
  *   - bf16 tensors are passed as uint16_t bit patterns, row-major, and every
@@ -30,8 +32,9 @@
  *     launch (a kernel grid past 2^32 work-items, which the dispatch packet
  *     cannot hold: row arrays past about 64 GiB) is one such error,
  *     MOE_ERR_ARG.
- *   - Only MOE_EAGER moe_route_build waits for the device (once, to read the
- *     row count back: "Eager vs captured").  Every other call, and every call in
+ *   - Only the eager route calls (moe_route_build and moe_route_dispatch in
+ *     MOE_EAGER mode) wait for the device, once each, to read the row count
+ *     back ("Eager vs captured").  Every other call, and every call in
  *     MOE_SYNC_FREE mode, is asynchronous, allocation-free and safe to record
  *     into a HIP graph ("Custom ops", "Buffers").
  *   - Calls that share output buffers must not overlap; calls on different
@@ -273,9 +276,10 @@ const char *moe_last_error(void);
 int moe_device_check(int device);
 
 /* Kernel timing, for callers that measure the library (a benchmark, a
- * profiler hook).  The next moe_route_build, moe_dispatch, moe_dispatch_fp8,
- * moe_combine, moe_combine_bwd or moe_dispatch_bwd call made on this host
- * thread times its own kernels into two HIP events:
+ * profiler hook).  The next moe_route_build, moe_route_dispatch,
+ * moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_bwd or
+ * moe_dispatch_bwd call made on this host thread times its own kernels into
+ * two HIP events:
  *   start_event  hipEvent_t (created by the caller, timing enabled) or NULL:
  *                takes the start time of the call's first kernel.
  *   stop_event   hipEvent_t or NULL: takes the end time of the call's last
