@@ -30,10 +30,11 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_HIDDEN, MOE_ERR_CAPACITY = 0, 1, 2, 3
 MOE_ERR_WORKSPACE, MOE_ERR_INDEX, MOE_ERR_HIP, MOE_ERR_DEVICE = 4, 5, 6, 7
 MOE_EAGER, MOE_SYNC_FREE = 0, 1
 MOE_FLAG_BAD_ID, MOE_FLAG_DUPLICATE, MOE_FLAG_ROWS_MISMATCH = 1, 2, 4
+MOE_NOALLOC_SCRATCH_BYTES = 4194304  # the fixed route scratch of moe_route_build_noalloc
 
 # Every symbol include/moe_mi355x.h declares.
 EXPORTS = ("moe_capacity_min", "moe_route_workspace_size", "moe_route_build",
-           "moe_route_dispatch", "moe_dispatch",
+           "moe_route_build_noalloc", "moe_route_dispatch", "moe_dispatch",
            "moe_dispatch_fp8", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
            "moe_last_error", "moe_device_check", "moe_time_next_call")
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_size.restype = ctypes.c_size_t
         L.moe_route_build.argtypes = [pd, vp, vp, vp, ph, vp, vp]
         L.moe_route_build.restype = ctypes.c_int
+        L.moe_route_build_noalloc.argtypes = [pd, vp, vp, vp, ph, vp, vp]
+        L.moe_route_build_noalloc.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_dispatch_fp8.argtypes = [pd, ph, vp, i32, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -224,7 +227,10 @@ class Handle:
         return int(self._host_words()[1])
 
 
-def alloc_handle(desc: Desc, device="cuda", with_map: bool = True) -> Handle:
+def alloc_handle(desc: Desc, device="cuda", with_map: bool = True,
+                 with_workspace: bool = True) -> Handle:
+    """Handle tensors for `desc`; with_workspace=False leaves the route
+    workspace out, as moe_route_build_noalloc requires."""
     T, E, EL, k = desc.T, desc.E, desc.num_local, desc.k
     return Handle(
         desc=desc,
@@ -234,7 +240,8 @@ def alloc_handle(desc: Desc, device="cuda", with_map: bool = True) -> Handle:
         row_of_slot=torch.empty((T, k), dtype=torch.int32, device=device),
         status=torch.empty(4, dtype=torch.int32, device=device),
         host_status=torch.zeros(4, dtype=torch.int32, pin_memory=True),
-        workspace=torch.empty(moe_route_workspace_size(desc), dtype=torch.uint8, device=device))
+        workspace=(torch.empty(moe_route_workspace_size(desc), dtype=torch.uint8, device=device)
+                   if with_workspace else None))
 
 
 # ---------------------------------------------------------------------------
@@ -263,6 +270,21 @@ def moe_route_build(desc: Desc, topk_idx: torch.Tensor, handle: Handle,
     href = handle.cref()
     return _check(lib().moe_route_build(ctypes.byref(desc), p_idx, p_w, p_probs, href,
                                         handle.host_status.data_ptr(), _stream(stream)))
+
+
+def moe_route_build_noalloc(desc: Desc, topk_idx: torch.Tensor, handle: Handle,
+                            topk_w: torch.Tensor | None = None,
+                            multihot_probs: torch.Tensor | None = None, stream=None) -> int:
+    """moe_route_build with the route's scratch in the library's fixed per-GPU
+    array: the handle must have no workspace (alloc_handle(...,
+    with_workspace=False)).  Nothing is allocated by the call."""
+    n = desc.T * desc.k
+    p_idx = _dev(topk_idx, "topk_idx", _I64 if desc.idx_is_i64 else _I32, n) if n else None
+    p_w = _dev(topk_w, "topk_w", _F32, n, optional=True)
+    p_probs = _dev(multihot_probs, "multihot_probs", _F32, desc.T * desc.E, optional=True)
+    return _check(lib().moe_route_build_noalloc(ctypes.byref(desc), p_idx, p_w, p_probs,
+                                                handle.cref(), handle.host_status.data_ptr(),
+                                                _stream(stream)))
 
 
 def moe_route_dispatch(desc: Desc, topk_idx: torch.Tensor, handle: Handle, x: torch.Tensor,

@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <chrono>
+#include <mutex>
 #include <thread>
 
 // The host's wait for the eager row count spins on a word of pinned memory;
@@ -262,15 +263,15 @@ size_t moe_route_workspace_size(const moe_desc *desc)
 
 namespace {
 
-// The route's checks and launches.  `a` keeps what route_wait needs.
-int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
-                 void *stream, moe::RouteArgs &a)
+// The route's argument rules; need_ws: the handle brings the workspace.
+int route_check(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                const float *multihot_probs, const moe_handle *handle,
+                const int32_t *host_status, bool need_ws)
 {
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
-    if ((rc = check_handle(desc, handle, true)) != MOE_OK)
+    if ((rc = check_handle(desc, handle, need_ws)) != MOE_OK)
         return rc;
     if (desc->T > 0 && !topk_idx)
         return fail(MOE_ERR_ARG, "topk_idx is NULL");
@@ -281,6 +282,18 @@ int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w
                                  "weights to write multihot_probs (pass weights to moe_dispatch)");
     if (desc->mode == MOE_EAGER && !host_status)
         return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
+    return MOE_OK;
+}
+
+// The route's checks and launches.  `a` keeps what route_wait needs.
+int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                 void *stream, moe::RouteArgs &a)
+{
+    int rc;
+    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, true)) !=
+        MOE_OK)
+        return rc;
     const WsLayout wl = ws_layout(desc);
     char *workspace = static_cast<char *>(handle->workspace);
 
@@ -359,6 +372,62 @@ int bad_id_check(const moe_desc *desc, const int32_t *host_status)
     return MOE_OK;
 }
 
+// moe_route_build's work (checks, launches, eager readback) for a handle
+// whose workspace is set.
+int route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                void *stream)
+{
+    moe::RouteArgs a;
+    int rc = route_launch(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream, a);
+    if (rc == MOE_OK && desc->mode == MOE_EAGER) {
+        if ((rc = route_wait(handle, host_status, stream, a)) == MOE_OK)
+            rc = bad_id_check(desc, host_status);
+    }
+    return rc == MOE_OK ? ok() : rc;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed route scratch of moe_route_build_noalloc, for callers that cannot
+// allocate.  One copy of the array per GPU, loaded with the library's code
+// object and held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is resolved once
+// per device (that device current) and only that address is handed to
+// kernels.  Nothing in it has to start at zero: every route writes each count
+// and flag word before reading it.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch_addr[kMaxDevices];
+
+int noalloc_scratch(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_DEVICE, "device %d: moe_route_build_noalloc serves devices 0..%d", dev,
+                    kMaxDevices - 1);
+    ScratchAddr &s = g_scratch_addr[dev];
+    std::call_once(s.once, [&s] {
+        s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+        if (s.err == hipSuccess && !s.ptr)
+            s.err = hipErrorInvalidSymbol;
+    });
+    if (s.err != hipSuccess)
+        return hip_fail(s.err, "hipGetSymbolAddress of the route scratch");
+    *out = s.ptr;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,13 +437,36 @@ int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *top
                     void *stream)
 {
     TimingScope timing_scope;
-    moe::RouteArgs a;
-    int rc = route_launch(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream, a);
-    if (rc == MOE_OK && desc->mode == MOE_EAGER) {
-        if ((rc = route_wait(handle, host_status, stream, a)) == MOE_OK)
-            rc = bad_id_check(desc, host_status);
-    }
-    return rc == MOE_OK ? ok() : rc;
+    return route_build(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream);
+}
+
+int moe_route_build_noalloc(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                            float *multihot_probs, const moe_handle *handle,
+                            int32_t *host_status, void *stream)
+{
+    TimingScope timing_scope;
+    int rc;
+    // every rule checked before the first HIP call
+    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, false)) !=
+        MOE_OK)
+        return rc;
+    if (handle->workspace || handle->workspace_bytes)
+        return fail(MOE_ERR_ARG, "moe_route_build_noalloc takes its scratch from the library's "
+                                 "fixed array: handle.workspace must be NULL and "
+                                 "workspace_bytes 0 (it would be ignored)");
+    const size_t need = ws_layout(desc).bytes;
+    if (need > kNoallocScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "this route needs %zu bytes of scratch, more than the "
+                                       "library's fixed %zu-byte array: use moe_route_build "
+                                       "with a workspace of moe_route_workspace_size bytes",
+                    need, kNoallocScratchBytes);
+    void *ws = nullptr;
+    if ((rc = noalloc_scratch(&ws)) != MOE_OK)
+        return rc;
+    moe_handle h = *handle;
+    h.workspace = ws;
+    h.workspace_bytes = kNoallocScratchBytes;
+    return route_build(desc, topk_idx, topk_w, multihot_probs, &h, host_status, stream);
 }
 
 int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *topk_w,

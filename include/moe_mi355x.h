@@ -19,9 +19,11 @@
  *   - All tensors are caller-allocated; the library never allocates device
  *     memory.  "device" pointers are HIP device (or managed) memory on the
  *     current device; "host" pointers are host memory.
- *   - State kept between calls, per host thread: the message of
+ *   - State kept between calls: per host thread, the message of
  *     moe_last_error() and a pending moe_time_next_call() request (consumed
- *     by the next call).  Nothing else outlives a call.
+ *     by the next call); per GPU, the fixed route scratch array of
+ *     moe_route_build_noalloc (with its device address, resolved on the
+ *     first such call).  Nothing else outlives a call.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every launch goes on that stream.
  *   - bf16 tensors are passed as uint16_t bit patterns, row-major, and every
@@ -32,11 +34,12 @@
  *     launch (a kernel grid past 2^32 work-items, which the dispatch packet
  *     cannot hold: row arrays past about 64 GiB) is one such error,
  *     MOE_ERR_ARG.
- *   - Only the eager route calls (moe_route_build and moe_route_dispatch in
- *     MOE_EAGER mode) wait for the device, once each, to read the row count
- *     back ("Eager vs captured").  Every other call, and every call in
- *     MOE_SYNC_FREE mode, is asynchronous, allocation-free and safe to record
- *     into a HIP graph ("Custom ops", "Buffers").
+ *   - Only the eager route calls (moe_route_build, moe_route_build_noalloc
+ *     and moe_route_dispatch in MOE_EAGER mode) wait for the device, once
+ *     each, to read the row count back ("Eager vs captured").  Every other
+ *     call, and every call in MOE_SYNC_FREE mode, is asynchronous,
+ *     allocation-free and safe to record into a HIP graph ("Custom ops",
+ *     "Buffers").
  *   - Calls that share output buffers must not overlap; calls on different
  *     buffers may run concurrently.
  */
@@ -142,6 +145,36 @@ size_t moe_route_workspace_size(const moe_desc *desc);
 int moe_route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
                     float *multihot_probs, const moe_handle *handle, int32_t *host_status,
                     void *stream);
+
+/* Bytes of the fixed route scratch array that moe_route_build_noalloc uses
+ * on each GPU (4 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES 4194304u
+
+/*
+ * moe_route_build for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  Its
+ * outputs, errors and waits are exactly moe_route_build's; the difference is
+ * where the route's scratch (per-block expert counts and flags) lives:
+ *   - in a fixed array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one
+ *     per GPU, held by every GPU the library runs on until the process ends;
+ *   - handle.workspace must be NULL and handle.workspace_bytes 0 (else
+ *     MOE_ERR_ARG: the buffer would be ignored);
+ *   - a route whose scratch, moe_route_workspace_size(desc), would exceed the
+ *     array returns MOE_ERR_WORKSPACE before anything is launched (with
+ *     512-thread route blocks that is about T*k*EL/128 bytes: 4 Mi slots of
+ *     top-k at 128 local experts, 256 Ki slots at 1024);
+ *   - the call allocates nothing, host or device.  The first call on a device
+ *     resolves the array's device address on the current device (a symbol
+ *     lookup, no allocation); make that first call outside graph capture.
+ * Every call on one GPU shares that GPU's array and finds there whatever the
+ * last call left (no word of it needs to start at zero: each route writes its
+ * scratch before reading it).  Calls whose kernels may overlap on one GPU
+ * (different streams or host threads without ordering between them) race on
+ * the array and give wrong results: order them, e.g. on one stream.
+ */
+int moe_route_build_noalloc(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                            float *multihot_probs, const moe_handle *handle,
+                            int32_t *host_status, void *stream);
 
 /*
  * Dispatch into the expanded layout ("Expanded layout"; "Eager vs captured").
@@ -276,10 +309,10 @@ const char *moe_last_error(void);
 int moe_device_check(int device);
 
 /* Kernel timing, for callers that measure the library (a benchmark, a
- * profiler hook).  The next moe_route_build, moe_route_dispatch,
- * moe_dispatch, moe_dispatch_fp8, moe_combine, moe_combine_bwd or
- * moe_dispatch_bwd call made on this host thread times its own kernels into
- * two HIP events:
+ * profiler hook).  The next moe_route_build, moe_route_build_noalloc,
+ * moe_route_dispatch, moe_dispatch, moe_dispatch_fp8, moe_combine,
+ * moe_combine_bwd or moe_dispatch_bwd call made on this host thread times
+ * its own kernels into two HIP events:
  *   start_event  hipEvent_t (created by the caller, timing enabled) or NULL:
  *                takes the start time of the call's first kernel.
  *   stop_event   hipEvent_t or NULL: takes the end time of the call's last

@@ -137,6 +137,42 @@ def test_workspace_rules():
     assert B.lib().moe_route_workspace_size(ctypes.byref(_desc(k=0))) == 0
 
 
+def test_noalloc_route_rules():
+    """moe_route_build_noalloc: a handle that brings a workspace, a route too
+    large for the fixed array, and the route's own rules are all refused
+    before any HIP call."""
+    L = B.lib()
+
+    def rc(d, h, w=None, probs=None, host=FAKE, idx=FAKE):
+        return L.moe_route_build_noalloc(ctypes.byref(d), idx, w, probs, ctypes.byref(h), host,
+                                         None)
+
+    d = _desc()
+    assert rc(d, _handle()) == B.MOE_ERR_ARG                      # a workspace it would ignore
+    assert "workspace" in B.last_error()
+    h = _handle(0)
+    h.workspace = None
+    h.workspace_bytes = 64
+    assert rc(d, h) == B.MOE_ERR_ARG
+    h.workspace_bytes = 0
+    big = _desc(T=40000, E=1024, num_local=1024, pad_multiple=1)  # 1250 blocks x 1024 counts
+    assert B.moe_route_workspace_size(big) > B.MOE_NOALLOC_SCRATCH_BYTES
+    assert rc(big, h) == B.MOE_ERR_WORKSPACE
+    assert "fixed" in B.last_error()
+    assert rc(d, h, w=FAKE) == B.MOE_ERR_ARG                      # weights with nothing to write
+    assert rc(d, h, probs=FAKE) == B.MOE_ERR_ARG                  # probs without weights
+    assert rc(d, h, host=None) == B.MOE_ERR_ARG                   # eager needs the host status
+    assert rc(d, h, idx=None) == B.MOE_ERR_ARG
+    assert rc(_desc(k=0), h) == B.MOE_ERR_ARG
+    assert rc(_desc(mode=B.MOE_SYNC_FREE, capacity=5), h) == B.MOE_ERR_CAPACITY
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES (\d+)u", src)
+    assert m and int(m.group(1)) == B.MOE_NOALLOC_SCRATCH_BYTES == 4 << 20
+
+
 def test_route_flag_pairs_are_never_ignored():
     d = _desc()
     assert route_rc(d, w=FAKE, probs=None) == B.MOE_ERR_ARG       # weights with nothing to write
