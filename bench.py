@@ -32,13 +32,23 @@ implementation": distinct layers back to back):
 
 Output: one JSON line.  `value` = algorithmic bytes of the step / wall time of
 the step (GB/s); `roofline` gives the dominant kernel's algorithmic GB/s
-(from its device time) against MI355X's 8 TB/s, and against the HIP runtime's
-1 GiB device copy timed on the same box (`hip_copy_GBps`, `frac_of_hip_copy`); `cpu_baseline` times the oracle on the
-host on a bounded sample of the same workload.  `next` times, outside the
-step, the FP8 dispatch and the dispatch backward on the same routings.  The
-metric is quoted at 4096 and at 16384 tokens, so `also` repeats the step
-(value and roofline) on the 16384-token, H = 4096 layers after the main one
-(`--companions`).
+(from its device time, average and spread over the timed steps) against
+MI355X's 8 TB/s, and against ceilings measured in the same run:
+  * `ceiling_GBps` / `frac_of_ceiling`: a one-shot copy of 1 GiB in address
+    order with non-temporal stores (libmoe_ceiling), the best plain stream
+    that moves as many bytes in as out;
+  * `write_bound_us` / `frac_of_write_bound`: the time the reference kernels
+    take to write the kernel's output rows alone, in the same layout and
+    store order and reading nothing (a token-major scatter of the data rows,
+    plus a one-shot fill of the sync-free zero tail);
+  * `hip_copy_GBps`: the HIP runtime's own 1 GiB device copy (torch copy_).
+`cpu_baseline` times the oracle on the host on a bounded sample of the same
+workload.  `next` times, outside the step, the FP8 dispatch and the dispatch
+backward on the same routings.  The metric is quoted at 4096 and at 16384
+tokens; `also` repeats the step (value, roofline, per-kernel times) on every
+other workload of the benchmark description after the main one
+(`--companions`): the tiny layer, the 16384-token H = 4096 layers and the
+skewed layer.
 """
 from __future__ import annotations
 
@@ -96,7 +106,7 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall budget of the oracle CPU-baseline leg (0 = skip)")
-    ap.add_argument("--companions", default="h4096_rank_share,backward_h4096",
+    ap.add_argument("--companions", default="tiny,h4096_rank_share,skewed,backward_h4096",
                     help="workloads also timed (value and roofline only) after the main one; "
                          "'' for none")
     ap.add_argument("--no-next", action="store_true",
@@ -127,11 +137,10 @@ def main():
     from combine_topk_idx_multihot_amd import inputs
 
     B.moe_device_check(0)
-    result, sets, wl = measure(args.workload, args, not args.no_next, torch, B, inputs)
-    # beside the 8 TB/s peak: the HIP runtime's own device copy on this machine
-    ceil = copy_ceiling(torch, torch.cuda.current_stream())
-    result["roofline"]["hip_copy_GBps"] = round(ceil, 1)
-    result["roofline"]["frac_of_hip_copy"] = round(result["roofline"]["achieved"] / ceil, 4)
+    # ceilings beside the 8 TB/s peak, measured on this machine before the layers
+    ceil = stream_ceilings(torch, torch.cuda.current_stream())
+    result, sets, wl = measure(args.workload, args, not args.no_next, torch, B, inputs, ceil)
+    result["ceilings"] = ceil
 
     # ---- CPU baseline: the oracle on the host, bounded sample ---------------
     if args.cpu_seconds > 0:
@@ -144,10 +153,10 @@ def main():
         result["also"] = {}
         for name in comp:
             torch.cuda.empty_cache()
-            r, s_, _ = measure(name, args, False, torch, B, inputs)
+            r, s_, _ = measure(name, args, False, torch, B, inputs, ceil)
             del s_
             result["also"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "config",
-                                                      "us_per_layer", "roofline")}
+                                                      "us_per_layer", "kernels", "roofline")}
 
     # ---- decode-sized layers replayed from a captured HIP graph --------------
     if not args.no_decode:
@@ -156,9 +165,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measure(name, args, with_next, torch, B, inputs):
+def measure(name, args, with_next, torch, B, inputs, ceil):
     """Warm up, take the per-kernel breakdown, then time K steps of workload
-    `name`.  Returns (result fields, buffer sets, workload)."""
+    `name`; `ceil` holds the stream ceilings of this machine.  Returns (result
+    fields, buffer sets, workload)."""
     wl = inputs.WORKLOADS[name]
     seed0 = args.seed if args.seed is not None else 1000 + list(inputs.WORKLOADS).index(wl.name) + 1
     dev = torch.device("cuda:0")
@@ -281,10 +291,20 @@ def measure(name, args, with_next, torch, B, inputs):
     step_bytes = float(np.mean([sum(facts[i % len(sets)][n] for n in names)
                                 for i in range(args.steps)]))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom_ms = float(np.mean([t.elapsed_ms() for t in dev_]))
+    dom_all = np.array([t.elapsed_ms() for t in dev_]) * 1e3
+    dom_ms = float(np.mean(dom_all)) * 1e-3
     dom_bytes = float(np.mean([facts[i % len(sets)][dominant] for i in range(args.steps)]))
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     dev_us = sum(kern[n]["avg_us"] for n in names)
+
+    # the write bound of every row kernel: the reference kernels writing the
+    # same output rows alone (same layout and store order, nothing read)
+    wb = write_bounds(wl, sets, facts, args.steps, torch, wl.k * wl.num_local >= 2 * wl.E)
+    for n in ("dispatch", "combine", "combine_bwd"):
+        kern[n]["frac_of_ceiling"] = round(kern[n]["GBps"] / ceil["copy_GBps"], 4)
+    for n in ("dispatch", "combine_bwd"):  # both write the layer's rows token-major
+        kern[n]["write_bound_us"] = wb
+        kern[n]["frac_of_write_bound"] = round(wb / kern[n]["avg_us"], 4)
 
     result = {
         "metric": METRIC,
@@ -310,8 +330,22 @@ def measure(name, args, with_next, torch, B, inputs):
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),
                      "traffic": None, "avg_us": round(dom_ms * 1e3, 2),
-                     "alg_bytes_per_launch": int(dom_bytes)},
+                     "spread_us": {"median": round(float(np.median(dom_all)), 2),
+                                   "min": round(float(dom_all.min()), 2),
+                                   "p10": round(float(np.percentile(dom_all, 10)), 2),
+                                   "p90": round(float(np.percentile(dom_all, 90)), 2),
+                                   "max": round(float(dom_all.max()), 2)},
+                     "frac_median": round(dom_bytes / (float(np.median(dom_all)) * 1e-6) / 1e9
+                                          / PEAK_GBS, 4),
+                     "alg_bytes_per_launch": int(dom_bytes),
+                     "ceiling_GBps": ceil["copy_GBps"],
+                     "frac_of_ceiling": round(dom_gbs / ceil["copy_GBps"], 4),
+                     "hip_copy_GBps": ceil["hip_copy_GBps"],
+                     "frac_of_hip_copy": round(dom_gbs / ceil["hip_copy_GBps"], 4)},
     }
+    if dominant in ("dispatch", "combine_bwd"):
+        result["roofline"]["write_bound_us"] = wb
+        result["roofline"]["frac_of_write_bound"] = round(wb / (dom_ms * 1e3), 4)
 
     result["roofline"]["traffic"] = measured_traffic(wl.name, dominant)
     if with_next:
@@ -483,26 +517,69 @@ def decode_graph(torch, B, inputs, reps=200):
     return out
 
 
-def copy_ceiling(torch, stream, mib=1024, reps=6):
-    """A plain device-to-device copy of `mib` MiB (torch's copy_, which is
-    the HIP runtime's copy kernel), timed live, in GB/s of bytes read +
-    written: a reference for a kernel that moves as many bytes in as out."""
-    n = mib << 20
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    a.fill_(1)
-    b.copy_(a)
+def _events_ms(torch, stream, fn, reps):
+    """Average ms of fn() over reps back-to-back calls, by events on `stream`."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
     for i in range(reps):
-        (b if i % 2 == 0 else a).copy_(a if i % 2 == 0 else b)
+        fn(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    return e0.elapsed_time(e1) / reps
+
+
+def stream_ceilings(torch, stream, mib=1024, reps=6):
+    """Plain streams over `mib` MiB buffers, timed live, in GB/s of bytes read +
+    written: the one-shot copy and zero fill of libmoe_ceiling (1 KiB per
+    wave, address order, non-temporal stores) and the HIP runtime's device
+    copy (torch copy_)."""
+    from combine_topk_idx_multihot_amd import ceiling as C
+
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    C.copy(a, b)
+    C.fill(b)
+    ms_copy = _events_ms(torch, stream, lambda i: C.copy(a if i % 2 == 0 else b,
+                                                          b if i % 2 == 0 else a), reps)
+    ms_fill = _events_ms(torch, stream, lambda i: C.fill(a if i % 2 == 0 else b), reps)
+    ms_hip = _events_ms(torch, stream, lambda i: (b if i % 2 == 0 else a).copy_(
+        a if i % 2 == 0 else b), reps)
     del a, b
-    return 2 * n / (ms * 1e-3) / 1e9
+    return {"copy_GBps": round(2 * n / (ms_copy * 1e-3) / 1e9, 1),
+            "fill_GBps": round(n / (ms_fill * 1e-3) / 1e9, 1),
+            "hip_copy_GBps": round(2 * n / (ms_hip * 1e-3) / 1e9, 1),
+            "bytes": n, "kind": "libmoe_ceiling one-shot copy and fill, 1 KiB per wave; "
+                                "torch copy_"}
+
+
+def write_bounds(wl, sets, facts, steps, torch, dense):
+    """us per layer for the reference kernels to write the layer's output rows
+    alone: a token-major scatter of zeros to the rows each set's handle names
+    (the dispatch's store order and segment size), plus, in sync-free mode, a
+    one-shot fill of the zero tail past the set's routed total.  Pad rows
+    (at most P - 1 per expert) are left out.  Rotates over the sets like the
+    step; average over `steps` calls."""
+    from combine_topk_idx_multihot_amd import ceiling as C
+
+    seg = 1 if dense else 2  # the dispatch's copy segment (1 KiB on dense layers)
+    stream = torch.cuda.current_stream()
+    totals = [int(st["h"].status[0]) for st in sets]
+
+    def one(i):
+        st = sets[i % len(sets)]
+        R = facts[i % len(sets)]["R"]
+        C.scatter(st["h"].row_of_slot, st["rows"][:R], seg_kib=seg)
+        tot = totals[i % len(sets)]
+        if wl.sync_free and tot < R:
+            C.fill(st["rows"][tot:R])
+
+    one(0)
+    return round(_events_ms(torch, stream, one, steps) * 1e3, 2)
 
 
 def oracle_steps(wl, a, budget_s, max_reps=500):

@@ -1,0 +1,76 @@
+"""Thin binding of libmoe_ceiling.so (C ABI in include/moe_ceiling.h): the
+reference kernels a benchmark times beside the library's own, on the same GPU
+and buffers.  Argument marshalling only; the library must have been built
+(``python -m combine_topk_idx_multihot_amd.build``)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import binding as _B
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_ceiling.so")
+
+# Every symbol include/moe_ceiling.h declares.
+EXPORTS = ("moe_ceiling_fill", "moe_ceiling_copy", "moe_ceiling_scatter")
+OK, ERR_ARG, ERR_HIP = 0, 1, 2
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m combine_topk_idx_multihot_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, i64, c = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+        L.moe_ceiling_fill.argtypes = [vp, sz, c, vp]
+        L.moe_ceiling_copy.argtypes = [vp, vp, sz, c, vp]
+        L.moe_ceiling_scatter.argtypes = [vp, i64, i32, i64, i32, vp, c, vp]
+        for n in EXPORTS:
+            getattr(L, n).restype = c
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def _buf(t: torch.Tensor, name: str) -> int:
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    return t.data_ptr()
+
+
+def fill(dst: torch.Tensor, piece_kib: int = 1, stream=None):
+    """Zero dst in address order, one wave per piece_kib KiB piece."""
+    _check(lib().moe_ceiling_fill(_buf(dst, "dst"), dst.numel() * dst.element_size(), piece_kib,
+                                  _B._stream(stream)), "moe_ceiling_fill")
+
+
+def copy(src: torch.Tensor, dst: torch.Tensor, piece_kib: int = 1, stream=None):
+    """dst[:] = src, in address order, one wave per piece_kib KiB piece."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(lib().moe_ceiling_copy(_buf(src, "src"), _buf(dst, "dst"), n, piece_kib,
+                                  _B._stream(stream)), "moe_ceiling_copy")
+
+
+def scatter(row_of_slot: torch.Tensor, rows: torch.Tensor, seg_kib: int = 1, stream=None):
+    """Zero every row of rows [R,H] bf16 that row_of_slot [T,k] int32 names,
+    token-major, one workgroup per token (the dispatch's store pattern without
+    its reads)."""
+    if row_of_slot.dtype != torch.int32 or row_of_slot.dim() != 2 or rows.dim() != 2:
+        raise ValueError("row_of_slot must be [T,k] int32 and rows [R,H]")
+    T, k = row_of_slot.shape
+    R, H = rows.shape
+    _check(lib().moe_ceiling_scatter(_buf(row_of_slot, "row_of_slot"), T, k, R, H,
+                                     _buf(rows, "rows"), seg_kib, _B._stream(stream)),
+           "moe_ceiling_scatter")

@@ -56,6 +56,8 @@
 // bits, except dw, whose fp64 summation order follows the dot segmentation
 // (within the dw tolerance of the parity tests):
 //   MOE_*_SEG         KiB of a row one wave moves per segment (1, 2 or 4);
+//                     MOE_COPY_SEG_DENSE is the bf16 dispatch's when most
+//                     tokens have local rows;
 //   MOE_MAX_WPT       most waves sharing one token's row in the row kernels;
 //   MOE_DOT_MAX_WPT   the same for the combine backward's dots;
 //   MOE_*_BATCH       rows whose loads or stores one wave keeps in flight;
@@ -69,6 +71,9 @@
 #endif
 #ifndef MOE_COPY_SEG
 #define MOE_COPY_SEG 2
+#endif
+#ifndef MOE_COPY_SEG_DENSE
+#define MOE_COPY_SEG_DENSE 1
 #endif
 #ifndef MOE_MAX_WPT
 #define MOE_MAX_WPT 4
@@ -111,7 +116,8 @@
 namespace moe {
 
 #define MOE_SEG_OK(x) ((x) == 1 || (x) == 2 || (x) == 4)
-static_assert(MOE_SEG_OK(MOE_COMBINE_SEG) && MOE_SEG_OK(MOE_COPY_SEG) && MOE_SEG_OK(MOE_DOT_SEG) &&
+static_assert(MOE_SEG_OK(MOE_COMBINE_SEG) && MOE_SEG_OK(MOE_COPY_SEG) &&
+                  MOE_SEG_OK(MOE_COPY_SEG_DENSE) && MOE_SEG_OK(MOE_DOT_SEG) &&
                   MOE_SEG_OK(MOE_DOT_SEG_SPARSE),
               "segment sizes are 1, 2 or 4 KiB");
 #undef MOE_SEG_OK
@@ -1036,7 +1042,6 @@ static int nch_of(const RowArgs &a) { return a.H >> 3; }
 void row_shape(RowArgs &a)
 {
     const int whole = chunks_per_lane(a.H);
-    const int cap = MOE_COPY_SEG;
     // Dots: a token with about k local rows gets its row dealt over up to
     // four waves in 1 KiB segments (more loads in flight at small T).  When
     // the local experts are a small share of all experts (fewer than two
@@ -1050,6 +1055,12 @@ void row_shape(RowArgs &a)
     a.dot_wpt = sparse ? 1 : (dnseg >= 4 && MOE_DOT_MAX_WPT >= 4 ? 4 : (dnseg >= 2 && MOE_DOT_MAX_WPT >= 2 ? 2 : 1));
     // combine backward with dw: periods of four tokens
     a.ndot_blocks = a.dw ? (a.T + kRowWaves - 1) / kRowWaves : 0;
+    // Copy segments: the bf16 dispatch of a layer whose local experts take
+    // most routes moves 1 KiB per wave and segment (measured on MI355X: T =
+    // 4096 dispatch 31.1 -> 29.9 us, T = 16384 255 -> 252 us); the FP8
+    // dispatch, the sparse share and the combine backward's copy keep 2 KiB
+    // (1 KiB measured slower or no faster there).
+    const int cap = (!a.rows_q && !a.dw && !sparse) ? MOE_COPY_SEG_DENSE : MOE_COPY_SEG;
     a.seg = whole < cap ? whole : cap;
     const int nch = a.H >> 3;
     const int nseg = (nch + a.seg * kWave - 1) / (a.seg * kWave);
