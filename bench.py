@@ -463,57 +463,77 @@ def cpu_model():
 DECODE_SHAPES = ((1, 2048), (256, 2048), (1, 4096), (256, 4096))
 
 
-def decode_graph(torch, B, inputs, reps=200):
-    """Decode-sized layers: route + dispatch + combine in sync-free mode
-    (worst-case rows, nothing read back to the host), E = 128, top-8, on a
-    one-rank share of 32 experts (expert parallelism over 4 GPUs), captured
-    once in a HIP graph and replayed `reps` times back to back.  us per layer
-    from events around the replays, for T tokens of hidden size H.  The
+def _graph_us(torch, fn, reps):
+    """fn(stream) captured once in a HIP graph, then replayed `reps` times
+    back to back: us per replay, from events around the replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(s)  # eager warm-up on the capture stream
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        g.capture_begin()
+        fn(s)
+        g.capture_end()
+        for _ in range(10):
+            g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del g
+    return us
+
+
+def decode_graph(torch, B, inputs, reps=100, layers=(1, 4, 16)):
+    """Decode-sized layers: route + dispatch (moe_route_dispatch) + combine in
+    sync-free mode (worst-case rows, nothing read back to the host), E = 128,
+    top-8, on a
+    one-rank share of 32 experts (expert parallelism over 4 GPUs).  As on the
+    pages' benchmark, distinct layers (each with its own routing, tokens and
+    buffers) run back to back: L of them are captured in one HIP graph and the
+    graph is replayed; us per layer = us per replay / L.  The pages time four
+    layers, so `us_per_layer` is L = 4; L = 1 and 16 are listed beside it.  A
+    graph replay has a fixed cost of its own on the host and GPU side, which
+    `graph_floor_us` shows: one replay of a graph of one trivial kernel.  The
     captured work is the library's kernels only (no exchange, no experts)."""
     E, k, EL, P = 128, 8, 32, 1
     out = {"shape": {"E": E, "k": k, "local_experts": EL, "pad_multiple": P,
-                     "mode": "sync_free", "replays": reps}}
+                     "mode": "sync_free", "replays": reps, "layers_per_graph": list(layers)}}
+    z = torch.zeros(256, device="cuda")
+    out["graph_floor_us"] = round(_graph_us(torch, lambda s: z.add_(1.0), reps), 2)
     for T, H in DECODE_SHAPES:
-        rng = np.random.default_rng([77, T, H])
-        idx, w = inputs.topk_softmax(T, E, k, rng)
-        C = B.moe_capacity_min(B.make_desc(T, k, E, 0, EL, P, B.MOE_EAGER, False, 0))
-        d = B.make_desc(T, k, E, 0, EL, P, B.MOE_SYNC_FREE, False, C)
-        idx_t = torch.from_numpy(idx).cuda()
-        w_t = torch.from_numpy(w).cuda()
-        gen = torch.Generator(device="cuda")
-        gen.manual_seed(77 * T + H)
-        x = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
-        h = B.alloc_handle(d)
-        rows = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
-        row_w = torch.empty(C, dtype=torch.float32, device="cuda")
-        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-        s = torch.cuda.Stream()
+        lay = []
+        for li in range(max(layers)):
+            rng = np.random.default_rng([77, T, H, li])
+            idx, w = inputs.topk_softmax(T, E, k, rng)
+            C = B.moe_capacity_min(B.make_desc(T, k, E, 0, EL, P, B.MOE_EAGER, False, 0))
+            d = B.make_desc(T, k, E, 0, EL, P, B.MOE_SYNC_FREE, False, C)
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(77 * T + H + 1000 * li)
+            lay.append(dict(
+                d=d, C=C, idx=torch.from_numpy(idx).cuda(), w=torch.from_numpy(w).cuda(),
+                x=torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16),
+                h=B.alloc_handle(d), rows=torch.empty((C, H), dtype=torch.bfloat16, device="cuda"),
+                row_w=torch.empty(C, dtype=torch.float32, device="cuda"),
+                y=torch.empty((T, H), dtype=torch.bfloat16, device="cuda")))
 
-        def layer():
-            B.moe_route_build(d, idx_t, h, stream=s)
-            B.moe_dispatch(d, h, x, H, C, rows, w_t, row_w, stream=s)
-            B.moe_combine(d, h, rows, H, C, y, stream=s)
+        def run(s, n, H=H, lay=lay):
+            for o in lay[:n]:
+                # route + dispatch in one call (one launch when T*k <= 16)
+                B.moe_route_dispatch(o["d"], o["idx"], o["h"], o["x"], H, o["rows"], o["w"],
+                                     None, o["row_w"], stream=s)
+                B.moe_combine(o["d"], o["h"], o["rows"], H, o["C"], o["y"], stream=s)
 
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            layer()
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            g.capture_begin()
-            layer()
-            g.capture_end()
-            for _ in range(10):
-                g.replay()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(s)
-            for _ in range(reps):
-                g.replay()
-            e1.record(s)
-        torch.cuda.synchronize()
-        out[f"T{T}_H{H}_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
-        del g
+        per = {L: round(_graph_us(torch, lambda s, L=L: run(s, L), reps) / L, 2) for L in layers}
+        out[f"T{T}_H{H}"] = {"us_per_layer": per[4] if 4 in per else per[layers[0]],
+                             **{f"L{L}_us_per_layer": v for L, v in per.items()}}
+        del lay
     return out
 
 

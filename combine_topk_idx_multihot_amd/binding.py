@@ -292,10 +292,12 @@ def moe_route_dispatch(desc: Desc, topk_idx: torch.Tensor, handle: Handle, x: to
                        multihot_probs: torch.Tensor | None = None,
                        row_w: torch.Tensor | None = None, row_token: torch.Tensor | None = None,
                        row_expert: torch.Tensor | None = None, stream=None) -> int:
-    """Eager route and dispatch in one call, into buffers of R_cap =
-    rows.shape[0] >= moe_capacity_min rows; the dispatch is queued before the
-    row count is read back.  Returns MOE_OK; handle.total is then the count,
-    and rows [0, total) are filled."""
+    """Route and dispatch in one call into buffers of R_cap = rows.shape[0]
+    rows.  Eager: R_cap >= moe_capacity_min, the dispatch is queued before
+    the row count is read back; handle.total is then the count and rows
+    [0, total) are filled.  Sync-free: R_cap = desc.capacity, nothing waits,
+    every row is written; a decode-sized route runs in the dispatch's own
+    launch."""
     T, k = desc.T, desc.k
     R_cap = rows.numel() // H if H > 0 else 0
     p_idx = _dev(topk_idx, "topk_idx", _I64 if desc.idx_is_i64 else _I32, T * k) if T * k else None
@@ -306,8 +308,6 @@ def moe_route_dispatch(desc: Desc, topk_idx: torch.Tensor, handle: Handle, x: to
     p_rw = _dev(row_w, "row_w", _F32, R_cap, optional=True)
     p_rt = _dev(row_token, "row_token", _I32, R_cap, optional=True)
     p_re = _dev(row_expert, "row_expert", _I32, R_cap, optional=True)
-    if p_w is None:
-        p_rw = None if T == 0 else p_rw
     return _check(lib().moe_route_dispatch(ctypes.byref(desc), p_idx, p_w, p_probs, handle.cref(),
                                            handle.host_status.data_ptr(), p_x, H, R_cap, p_rows,
                                            p_rw, p_rt, p_re, _stream(stream)))

@@ -285,18 +285,13 @@ int route_check(const moe_desc *desc, const void *topk_idx, const float *topk_w,
     return MOE_OK;
 }
 
-// The route's checks and launches.  `a` keeps what route_wait needs.
-int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
-                 void *stream, moe::RouteArgs &a)
+// The route's kernel arguments (device side only; the eager host status is
+// set up by route_launch).
+moe::RouteGeom route_args(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                          float *multihot_probs, const moe_handle *handle, moe::RouteArgs &a)
 {
-    int rc;
-    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, true)) !=
-        MOE_OK)
-        return rc;
     const WsLayout wl = ws_layout(desc);
     char *workspace = static_cast<char *>(handle->workspace);
-
     const moe::RouteGeom g = moe::route_geom(desc->T, desc->k, desc->num_local);
     a.idx = topk_idx;
     a.w = topk_w;
@@ -318,6 +313,19 @@ int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w
     a.nblk = g.nblk;
     a.idx_i64 = desc->idx_is_i64;
     a.host_status = nullptr;
+    return g;
+}
+
+// The route's checks and launches.  `a` keeps what route_wait needs.
+int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
+                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
+                 void *stream, moe::RouteArgs &a)
+{
+    int rc;
+    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, true)) !=
+        MOE_OK)
+        return rc;
+    const moe::RouteGeom g = route_args(desc, topk_idx, topk_w, multihot_probs, handle, a);
     if (desc->mode == MOE_EAGER) {
         // Pinned (device-visible) host memory: the kernel writes the status
         // there directly; pageable memory takes a copy after the kernels.
@@ -479,14 +487,15 @@ int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *
     // every argument of both halves is checked before anything is launched
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
-    if (desc->mode != MOE_EAGER)
-        return fail(MOE_ERR_ARG, "moe_route_dispatch is for eager mode (sync-free calls never wait: "
-                                 "queue moe_route_build and moe_dispatch)");
+    const bool eager = desc->mode == MOE_EAGER;
     if ((rc = check_handle(desc, handle, true)) != MOE_OK)
         return rc;
     if ((rc = check_hidden(H)) != MOE_OK)
         return rc;
-    if (R_cap < cap_min(desc) || R_cap > kI32Max)
+    if (!eager && R_cap != desc->capacity)
+        return fail(MOE_ERR_ARG, "sync-free mode: R_cap must equal desc->capacity (%lld), got %lld",
+                    (long long)desc->capacity, (long long)R_cap);
+    if (eager && (R_cap < cap_min(desc) || R_cap > kI32Max))
         return fail(MOE_ERR_CAPACITY, "R_cap %lld must hold the worst case T*min(k,EL) + EL*(P-1) = "
                                       "%lld rows (and fit in int32)",
                     (long long)R_cap, (long long)cap_min(desc));
@@ -494,20 +503,40 @@ int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *
         return fail(MOE_ERR_ARG, "x must be a non-NULL, 16-byte aligned [T,H] bf16 tensor");
     if (R_cap > 0 && (!rows || !aligned16(rows)))
         return fail(MOE_ERR_ARG, "rows must be a non-NULL, 16-byte aligned [R_cap,H] bf16 tensor");
-    if ((multihot_probs || row_w) && !topk_w)
+    if ((multihot_probs || row_w) && !topk_w && desc->T > 0)
         return fail(MOE_ERR_ARG, "multihot_probs or row_w requested without topk_w");
     if (topk_w && !multihot_probs && !row_w)
         return fail(MOE_ERR_ARG, "topk_w given but neither multihot_probs nor row_w is requested");
-    if (!host_status)
+    if (eager && !host_status)
         return fail(MOE_ERR_ARG, "eager mode needs host_status (int32[4]) to return the row count");
-    // the dispatch, bounded by the buffers' capacity: it writes the rows
-    // [0, total) and leaves the rest
+    if (desc->T > 0 && !topk_idx)
+        return fail(MOE_ERR_ARG, "topk_idx is NULL");
+    // eager: the dispatch, bounded by the buffers' capacity, writes the rows
+    // [0, total) and leaves the rest; sync-free: every row, as moe_dispatch
     const moe::RowArgs ra = dispatch_args(desc, handle, x, H, row_w ? topk_w : nullptr, R_cap, rows,
-                                          nullptr, nullptr, row_w, row_token, row_expert, true);
+                                          nullptr, nullptr, row_w, row_token, row_expert, eager);
     if (!moe::move_rows_fits(ra))
         return hip_fail(hipErrorInvalidConfiguration, "dispatch");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
 
     moe::RouteArgs a;
+    if (!eager) {
+        // nothing waits; a route of at most kTinySlots slots goes into the
+        // dispatch's own launch
+        route_args(desc, topk_idx, multihot_probs ? topk_w : nullptr, multihot_probs, handle, a);
+        if (moe::route_move_tiny_fits(ra, a)) {
+            if ((e = moe::launch_route_move_tiny(ra, a, s)) != hipSuccess)
+                return hip_fail(e, "route and dispatch launch");
+            return ok();
+        }
+        if ((rc = route_launch(desc, topk_idx, multihot_probs ? topk_w : nullptr, multihot_probs,
+                               handle, host_status, stream, a)) != MOE_OK)
+            return rc;
+        if ((e = moe::launch_move_rows(ra, s)) != hipSuccess)
+            return hip_fail(e, "dispatch launch");
+        return ok();
+    }
     if ((rc = route_launch(desc, topk_idx, multihot_probs ? topk_w : nullptr, multihot_probs, handle,
                            host_status, stream, a)) != MOE_OK)
         return rc;
@@ -515,8 +544,7 @@ int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *
     if (!a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
         return rc;
     // the dispatch, queued before the row count is known
-    hipError_t e = moe::launch_move_rows(ra, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
+    if ((e = moe::launch_move_rows(ra, s)) != hipSuccess)
         return hip_fail(e, "dispatch launch");
     if (a.host_status && (rc = route_wait(handle, host_status, stream, a)) != MOE_OK)
         return rc;

@@ -89,6 +89,21 @@ void row_shape(RowArgs &a);
 bool move_rows_fits(const RowArgs &a); // launch_move_rows' grids within kMaxRowBlocks
 hipError_t launch_move_rows(const RowArgs &a, hipStream_t s);
 
+// Decode-sized sync-free route and dispatch in one launch: every workgroup
+// computes the route of at most kTinySlots slots (T*k <= 16) in its own LDS,
+// workgroup 0 publishes the handle.  Only for sync-free bf16 dispatches whose
+// zero tail is filled by the rows' launch and whose multihot map has at most
+// kTinyMapEntries entries; route_move_tiny_fits says whether `a` and `r`
+// qualify, and the launcher refuses (hipErrorInvalidConfiguration) otherwise.
+constexpr int64_t kTinyMapEntries = 65536;
+#ifndef MOE_TINY_SLOTS
+#define MOE_TINY_SLOTS 16
+#endif
+constexpr int kTinySlots = MOE_TINY_SLOTS;  // at most 64 (one wave)
+static_assert(kTinySlots >= 0 && kTinySlots <= kWave, "tiny routes fit one wave");
+bool route_move_tiny_fits(const RowArgs &a, const RouteArgs &r);
+hipError_t launch_route_move_tiny(const RowArgs &a, const RouteArgs &r, hipStream_t s);
+
 struct CombineArgs {
     const uint16_t *Y;          // [R,H]
     void *out;                  // [T,H] bf16 or f32

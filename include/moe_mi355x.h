@@ -198,29 +198,39 @@ int moe_dispatch(const moe_desc *desc, const moe_handle *handle, const uint16_t 
                  int32_t *row_token, int32_t *row_expert, void *stream);
 
 /*
- * Eager route and dispatch in one call ("Eager vs captured": the eager mode's
- * one readback, taken off the device's critical path).  For callers whose
- * row buffers hold the worst case, moe_capacity_min(desc) rows, such as a
- * loop over persistent buffers.  The dispatch is queued right behind the
- * route, before the row count is read back.  So the device goes from the
- * route to the dispatch without waiting for the host, while the host waits
- * for the count as moe_route_build does.
- *   desc.mode      MOE_EAGER (sync-free calls never wait: use the two calls).
- *   topk_idx, multihot_probs, handle, host_status: as for moe_route_build.
+ * Route and dispatch in one call ("Eager vs captured").  Every argument of
+ * both halves is checked before anything is launched; the handle's
+ * workspace rules are moe_route_build's.
+ *   topk_idx, multihot_probs, handle: as for moe_route_build.
  *   topk_w         device [T,k] fp32 or NULL: read for multihot_probs and for
  *                  row_w, and needed by either.
  *   x, H           as for moe_dispatch.
- *   R_cap          rows the buffers hold, >= moe_capacity_min(desc), else
- *                  MOE_ERR_CAPACITY.
  *   rows           device [R_cap,H] bf16 out; row_w, row_token, row_expert:
  *                  device [R_cap] out or NULL.
- * On return host_status holds {total, flags, data rows} as after
- * moe_route_build, and rows [0, total) of every output are exactly what
- * moe_dispatch with R = total writes.  Rows at or past total are not
- * written.  Every argument of both halves is checked before anything is
- * launched.  An out-of-range id returns MOE_ERR_INDEX after the readback, as
- * moe_route_build does; the dispatch has then still run, with such slots
- * treated as empty.
+ * MOE_EAGER (the eager mode's one readback, taken off the device's critical
+ * path), for callers whose row buffers hold the worst case, such as a loop
+ * over persistent buffers:
+ *   R_cap          rows the buffers hold, >= moe_capacity_min(desc), else
+ *                  MOE_ERR_CAPACITY.
+ *   host_status    as for moe_route_build.
+ * The dispatch is queued right behind the route, before the row count is
+ * read back.  So the device goes from the route to the dispatch without
+ * waiting for the host, while the host waits for the count as
+ * moe_route_build does.  On return host_status holds {total, flags, data
+ * rows} as after moe_route_build, and rows [0, total) of every output are
+ * exactly what moe_dispatch with R = total writes.  Rows at or past total
+ * are not written.  An out-of-range id returns MOE_ERR_INDEX after the
+ * readback, as moe_route_build does; the dispatch has then still run, with
+ * such slots treated as empty.
+ * MOE_SYNC_FREE (nothing waits; safe to record into a HIP graph):
+ *   R_cap          must equal desc->capacity (else MOE_ERR_ARG).
+ *   host_status    unused, may be NULL.
+ * The handle and every row are exactly what moe_route_build followed by
+ * moe_dispatch with R = capacity write.  A route of at most 16 slots
+ * (T*k <= 16: decode sizes) whose row array is small (at most 32 MiB) and
+ * whose multihot map has at most 65536 entries runs in the dispatch's own
+ * launch: each workgroup computes that small route itself, so the pair
+ * costs one kernel launch instead of two.
  */
 int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
                        float *multihot_probs, const moe_handle *handle, int32_t *host_status,

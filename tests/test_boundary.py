@@ -297,12 +297,17 @@ def rd_rc(d, H=2048, R_cap=None, idx=FAKE, w=None, probs=None, host=FAKE, x=FAKE
 
 
 def test_route_dispatch_argument_rules():
-    """The eager route-and-dispatch checks the arguments of both halves before
-    it launches anything."""
+    """The route-and-dispatch checks the arguments of both halves before it
+    launches anything, in both modes."""
     d = _desc()
     cap = B.lib().moe_capacity_min(ctypes.byref(d))
     sf = _desc(mode=B.MOE_SYNC_FREE, capacity=cap)
-    assert rd_rc(sf) == B.MOE_ERR_ARG and "eager" in B.last_error()
+    # sync-free: R_cap is the capacity, the host status is not needed
+    assert rd_rc(sf, R_cap=cap + 1) == B.MOE_ERR_ARG and "capacity" in B.last_error()
+    assert rd_rc(sf, x=None) == B.MOE_ERR_ARG
+    assert rd_rc(sf, idx=None) == B.MOE_ERR_ARG
+    assert rd_rc(sf, H=384) == B.MOE_ERR_HIDDEN
+    assert rd_rc(sf, w=FAKE) == B.MOE_ERR_ARG
     assert rd_rc(d, R_cap=cap - 1) == B.MOE_ERR_CAPACITY
     assert rd_rc(d, H=384) == B.MOE_ERR_HIDDEN
     assert rd_rc(d, host=None) == B.MOE_ERR_ARG
