@@ -141,6 +141,9 @@ def main():
     ceil = stream_ceilings(torch, torch.cuda.current_stream())
     result, sets, wl = measure(args.workload, args, not args.no_next, torch, B, inputs, ceil)
     result["ceilings"] = ceil
+    # the row kernels' workgroup numbering assumes workgroup j runs on XCD j mod 8
+    from combine_topk_idx_multihot_amd import ceiling as C
+    result["xcd_round_robin"] = C.xcd_round_robin()
 
     # ---- CPU baseline: the oracle on the host, bounded sample ---------------
     if args.cpu_seconds > 0:

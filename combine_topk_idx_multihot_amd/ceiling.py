@@ -14,7 +14,7 @@ from . import binding as _B
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_ceiling.so")
 
 # Every symbol include/moe_ceiling.h declares.
-EXPORTS = ("moe_ceiling_fill", "moe_ceiling_copy", "moe_ceiling_scatter")
+EXPORTS = ("moe_ceiling_fill", "moe_ceiling_copy", "moe_ceiling_scatter", "moe_ceiling_xcd_map")
 OK, ERR_ARG, ERR_HIP = 0, 1, 2
 
 _lib = None
@@ -31,6 +31,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ceiling_fill.argtypes = [vp, sz, c, vp]
         L.moe_ceiling_copy.argtypes = [vp, vp, sz, c, vp]
         L.moe_ceiling_scatter.argtypes = [vp, i64, i32, i64, i32, vp, c, vp]
+        L.moe_ceiling_xcd_map.argtypes = [vp, i32, vp]
         for n in EXPORTS:
             getattr(L, n).restype = c
         _lib = L
@@ -74,3 +75,21 @@ def scatter(row_of_slot: torch.Tensor, rows: torch.Tensor, seg_kib: int = 1, str
     _check(lib().moe_ceiling_scatter(_buf(row_of_slot, "row_of_slot"), T, k, R, H,
                                      _buf(rows, "rows"), seg_kib, _B._stream(stream)),
            "moe_ceiling_scatter")
+
+
+def xcd_map(nblocks: int = 4096, stream=None) -> torch.Tensor:
+    """The XCD each of `nblocks` workgroups ran on (int32 on the GPU)."""
+    out = torch.full((nblocks,), -1, dtype=torch.int32, device="cuda")
+    _check(lib().moe_ceiling_xcd_map(_buf(out, "out"), nblocks, _B._stream(stream)),
+           "moe_ceiling_xcd_map")
+    return out
+
+
+def xcd_round_robin(nblocks: int = 4096) -> dict:
+    """Whether workgroup j ran on XCD j mod (number of XCDs seen), as the
+    library's row kernels assume."""
+    m = xcd_map(nblocks).cpu().numpy()
+    n = len(set(m.tolist()))
+    j = list(range(nblocks))
+    match = sum(1 for i in j if m[i] == i % n) / nblocks
+    return {"xcds_seen": n, "blocks": nblocks, "frac_j_mod_xcds": round(match, 4)}

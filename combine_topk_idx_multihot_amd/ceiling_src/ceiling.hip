@@ -14,6 +14,10 @@
 //            segments of seg_kib KiB to every row the token's slots name,
 //            exactly the destinations (and the order of destinations in
 //            flight) of the dispatch's row stores, with no source reads.
+//   xcd_map  the accelerator complex die (XCD) each workgroup of a grid ran
+//            on, read from the wave's XCC_ID hardware register: the row
+//            kernels number their workgroups on the assumption that
+//            workgroup j runs on XCD j mod 8.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,6 +94,16 @@ __global__ void __launch_bounds__(kWave *kWaves) k_scatter(const int32_t *__rest
             }
         }
     }
+}
+
+// XCC_ID hardware register (id 20), bits [3:0]: s_getreg's immediate is
+// (size - 1) << 11 | offset << 6 | id.
+constexpr int kXccIdReg = (3 << 11) | (0 << 6) | 20;
+
+__global__ void __launch_bounds__(kWave *kWaves) k_xcd_map(int32_t *__restrict__ out)
+{
+    if (threadIdx.x == 0)
+        out[blockIdx.x] = __builtin_amdgcn_s_getreg(kXccIdReg);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -176,6 +190,17 @@ int moe_ceiling_scatter(const int32_t *row_of_slot, int64_t T, int32_t k, int64_
     case 2: hipLaunchKernelGGL(k_scatter<2>, g, b, 0, s, row_of_slot, T, k, R, nch, d); break;
     default: hipLaunchKernelGGL(k_scatter<4>, g, b, 0, s, row_of_slot, T, k, R, nch, d); break;
     }
+    return launched();
+}
+
+int moe_ceiling_xcd_map(int32_t *out, int32_t nblocks, void *stream)
+{
+    if (nblocks < 0 || (nblocks > 0 && !out))
+        return MOE_CEILING_ERR_ARG;
+    if (nblocks == 0)
+        return MOE_CEILING_OK;
+    hipLaunchKernelGGL(k_xcd_map, dim3(static_cast<unsigned>(nblocks)), dim3(kWave * kWaves), 0,
+                       static_cast<hipStream_t>(stream), out);
     return launched();
 }
 

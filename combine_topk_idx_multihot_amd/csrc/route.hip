@@ -305,13 +305,14 @@ __device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, i
     }
     __syncthreads();
     if (a.status && a.host_status && tid == 0) {
-        // words 0..2 first, then word 3 (the host waits for it to turn 0)
+        // words 0..2 first, then word 3 (the host waits for it to turn 0),
+        // whose release store orders the three before it at system scope
+        // (system-scope fences around the stores measured 0.3 us slower per
+        // route on MI355X and are not needed for that order)
 #pragma unroll
         for (int i = 0; i < 3; ++i)
             __hip_atomic_store(a.host_status + i, st[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        __threadfence_system();
         __hip_atomic_store(a.host_status + 3, st[3], __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-        __threadfence_system();
     }
 }
 

@@ -46,6 +46,14 @@ int moe_ceiling_copy(const void *src, void *dst, size_t bytes, int piece_kib, vo
 int moe_ceiling_scatter(const int32_t *row_of_slot, int64_t T, int32_t k, int64_t R, int32_t H,
                         void *rows, int seg_kib, void *stream);
 
+/* out[j] = the XCD (accelerator complex die, 0..7 on MI355X) that workgroup
+ * j of a grid of `nblocks` workgroups of 256 threads (the row kernels'
+ * size) ran on, from its first wave's
+ * XCC_ID hardware register.  The library's row kernels assume workgroup j
+ * runs on XCD j mod 8 (the combine backward's copy and dot workgroups of one
+ * token period share an XCD's L2); this checks it on the running GPU. */
+int moe_ceiling_xcd_map(int32_t *out, int32_t nblocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

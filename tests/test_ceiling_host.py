@@ -39,3 +39,5 @@ def test_refusals():
     assert sc(FAKE, 10, 8, 100, 256, FAKE, 3, None) == C.ERR_ARG          # segment size
     assert sc(FAKE, -1, 8, 100, 256, FAKE, 1, None) == C.ERR_ARG
     assert sc(None, 0, 8, 100, 256, None, 1, None) == C.OK                # no token
+    assert L.moe_ceiling_xcd_map(None, 4, None) == C.ERR_ARG
+    assert L.moe_ceiling_xcd_map(None, 0, None) == C.OK

@@ -49,3 +49,14 @@ def test_scatter_zeroes_exactly_the_named_rows(seg):
     got = rows.float().cpu().numpy()
     assert (got[named] == 0).all()
     assert (got[~named] == 1.5).all()
+
+
+def test_workgroups_run_on_xcd_j_mod_8():
+    """The combine backward numbers its workgroups so that the copy and dot
+    workgroups of one token period land on one XCD, assuming workgroup j runs
+    on XCD j mod 8 (MI355X in its one-partition mode).  Checked on this GPU
+    from each workgroup's XCC_ID register."""
+    m = C.xcd_map(8192).cpu().numpy()
+    say(f"[xcd] XCDs seen: {sorted(set(m.tolist()))}")
+    assert set(m.tolist()) == set(range(8))
+    np.testing.assert_array_equal(m, np.arange(8192) % 8)

@@ -255,6 +255,8 @@ EDGE = [
     ("large_route_128_local_sync_free", 33000, 128, 8, 0, 128, 1, True, 256, 0.0, False, False),
     ("large_route_share_sync_free", 33000, 128, 8, 16, 16, 4, True, 256, 0.02, True, False),
     ("large_route_dups_bad_ids", 33000, 128, 8, 0, 128, 4, False, 256, 0.05, True, True),
+    ("large_route_1024_local_132_blocks", 4200, 1024, 8, 0, 1024, 1, True, 256, 0.02, True,
+     False),
 ]
 
 
