@@ -2,7 +2,7 @@
 byte model held against the HBM traffic the hardware counters measured.
 
 profiles/traffic.json holds rocprofv3 FETCH_SIZE / WRITE_SIZE per launch of
-every call on the four measured layers, scaled by a plain copy of known size.
+every call on the five measured layers, scaled by a plain copy of known size.
 The byte model counts each input once and each output once.  The row kernels
 re-read and over-write nothing, so the two must agree closely; a mistake in
 the model (a dropped metadata array, rows counted for the wrong R, the FP8
@@ -66,15 +66,20 @@ def test_more_than_one_gpu_is_refused():
 def test_byte_model_matches_counted_traffic(wname):
     meas = traffic()["workloads"][wname]
     model = model_bytes(wname)
+    # Each launch also fetches its code and arguments (tens of KB that the
+    # counters see and the model does not): only a layer of well under a MB
+    # per call, the tiny one, notices, hence the absolute slack.
+    slack = 256 << 10
     for call in ROW_CALLS:
-        ratio = meas[call]["bytes"] / model[call]
-        # the row kernels: within 2.5 % (measured 1.000 to 1.021)
-        assert abs(ratio - 1.0) <= 0.025, (wname, call, ratio)
+        diff = meas[call]["bytes"] - model[call]
+        # the row kernels: within 2.5 % (measured 1.000 to 1.021 on the
+        # large layers)
+        assert abs(diff) <= max(0.025 * model[call], slack), (wname, call, diff / model[call])
     # the route's two passes hand the packed slot ranks and the per-block
     # counts through memory, which the model does not count: measured 1.10 to
     # 1.24 times the model, a few MB at most
     r = meas["route"]["bytes"] / model["route"]
-    assert 1.0 <= r <= 1.3, (wname, r)
+    assert 1.0 <= r and meas["route"]["bytes"] <= 1.3 * model["route"] + slack, (wname, r)
 
 
 def test_traffic_is_null_once_sources_change(monkeypatch):
