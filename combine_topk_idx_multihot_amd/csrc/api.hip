@@ -103,31 +103,56 @@ int check_desc(const moe_desc *d)
 }
 
 struct WsLayout {
-    size_t counts_off, flags_off, bytes;
+    size_t counts_off, flags_off, pairs_off, bytes;
+    bool pairs;          // the route writes its row list at pairs_off
+    moe::PairGeom pg;
 };
 
-// The handle's workspace: route scratch, per-block expert counts and flags.
-WsLayout ws_layout(const moe_desc *d)
+// The handle's workspace: route scratch (per-block expert counts and flags)
+// and, for dense routing, the route's row list, which the dispatch and the
+// combine backward read.  with_pairs = false: the scratch alone (the fixed
+// array of moe_route_build_noalloc).
+WsLayout ws_layout(const moe_desc *d, bool with_pairs = true)
 {
     const moe::RouteGeom g = moe::route_geom(d->T, d->k, d->num_local);
     auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     WsLayout w;
     w.counts_off = 0;
     w.flags_off = up(static_cast<size_t>(g.nblk) * d->num_local * sizeof(int32_t));
-    w.bytes = w.flags_off + up(static_cast<size_t>(g.nblk) * sizeof(int32_t));
+    w.pairs_off = w.flags_off + up(static_cast<size_t>(g.nblk) * sizeof(int32_t));
+    w.bytes = w.pairs_off;
+    w.pairs = with_pairs && moe::pairs_form(d->T, d->k, d->E, d->num_local, g.tokens_per_block,
+                                            g.nblk);
+    if (w.pairs) {
+        w.pg = moe::pair_geom(d->T, d->k, d->num_local, g.tokens_per_block, g.nblk);
+        w.bytes += up(static_cast<size_t>(w.pg.entries) * sizeof(int2));
+    }
     if (w.bytes == 0)
         w.bytes = 256;
     return w;
 }
 
-// The workspace is scratch of moe_route_build alone; the calls after it never
-// read it, so only route_build checks it (need_ws).
-int check_handle(const moe_desc *d, const moe_handle *h, bool need_ws = false)
+// The route's row list in a handle, for the row kernels: present when the
+// description's route writes one and the handle brings a workspace large
+// enough to hold it (handles without a workspace walk tokens).
+const int2 *handle_pairs(const moe_desc *d, const moe_handle *h, moe::PairGeom &pg)
+{
+    const WsLayout wl = ws_layout(d);
+    if (!wl.pairs || !h->workspace || h->workspace_bytes < wl.bytes)
+        return nullptr;
+    pg = wl.pg;
+    return reinterpret_cast<const int2 *>(static_cast<const char *>(h->workspace) + wl.pairs_off);
+}
+
+// The route needs the workspace (need_ws; with room for its row list unless
+// pairs is false); the calls after it read the row list when it is there and
+// walk tokens otherwise, so only the route checks the workspace.
+int check_handle(const moe_desc *d, const moe_handle *h, bool need_ws = false, bool pairs = true)
 {
     if (!h)
         return fail(MOE_ERR_ARG, "handle is NULL");
     if (need_ws) {
-        const WsLayout wl = ws_layout(d);
+        const WsLayout wl = ws_layout(d, pairs);
         if (!h->workspace || h->workspace_bytes < wl.bytes)
             return fail(MOE_ERR_WORKSPACE, "handle.workspace needs %zu bytes (got %zu%s)", wl.bytes,
                         h->workspace_bytes, h->workspace ? "" : ", NULL");
@@ -223,6 +248,7 @@ moe::RowArgs dispatch_args(const moe_desc *desc, const moe_handle *handle, const
     a.E_total = desc->E;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
+    a.pairs = rows_q ? nullptr : handle_pairs(desc, handle, a.pg);
     moe::row_shape(a);
     return a;
 }
@@ -266,12 +292,12 @@ namespace {
 // The route's argument rules; need_ws: the handle brings the workspace.
 int route_check(const moe_desc *desc, const void *topk_idx, const float *topk_w,
                 const float *multihot_probs, const moe_handle *handle,
-                const int32_t *host_status, bool need_ws)
+                const int32_t *host_status, bool need_ws, bool pairs = true)
 {
     int rc;
     if ((rc = check_desc(desc)) != MOE_OK)
         return rc;
-    if ((rc = check_handle(desc, handle, need_ws)) != MOE_OK)
+    if ((rc = check_handle(desc, handle, need_ws, pairs)) != MOE_OK)
         return rc;
     if (desc->T > 0 && !topk_idx)
         return fail(MOE_ERR_ARG, "topk_idx is NULL");
@@ -286,11 +312,13 @@ int route_check(const moe_desc *desc, const void *topk_idx, const float *topk_w,
 }
 
 // The route's kernel arguments (device side only; the eager host status is
-// set up by route_launch).
+// set up by route_launch).  pairs: write the row list (when the description
+// has one) into the workspace.
 moe::RouteGeom route_args(const moe_desc *desc, const void *topk_idx, const float *topk_w,
-                          float *multihot_probs, const moe_handle *handle, moe::RouteArgs &a)
+                          float *multihot_probs, const moe_handle *handle, moe::RouteArgs &a,
+                          bool pairs = true)
 {
-    const WsLayout wl = ws_layout(desc);
+    const WsLayout wl = ws_layout(desc, pairs);
     char *workspace = static_cast<char *>(handle->workspace);
     const moe::RouteGeom g = moe::route_geom(desc->T, desc->k, desc->num_local);
     a.idx = topk_idx;
@@ -313,19 +341,24 @@ moe::RouteGeom route_args(const moe_desc *desc, const void *topk_idx, const floa
     a.nblk = g.nblk;
     a.idx_i64 = desc->idx_is_i64;
     a.host_status = nullptr;
+    a.pairs = nullptr;
+    if (wl.pairs) {
+        a.pairs = reinterpret_cast<int2 *>(workspace + wl.pairs_off);
+        a.pg = wl.pg;
+    }
     return g;
 }
 
 // The route's checks and launches.  `a` keeps what route_wait needs.
 int route_launch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
                  float *multihot_probs, const moe_handle *handle, int32_t *host_status,
-                 void *stream, moe::RouteArgs &a)
+                 void *stream, moe::RouteArgs &a, bool pairs = true)
 {
     int rc;
-    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, true)) !=
-        MOE_OK)
+    if ((rc = route_check(desc, topk_idx, topk_w, multihot_probs, handle, host_status, true,
+                          pairs)) != MOE_OK)
         return rc;
-    const moe::RouteGeom g = route_args(desc, topk_idx, topk_w, multihot_probs, handle, a);
+    const moe::RouteGeom g = route_args(desc, topk_idx, topk_w, multihot_probs, handle, a, pairs);
     if (desc->mode == MOE_EAGER) {
         // Pinned (device-visible) host memory: the kernel writes the status
         // there directly; pageable memory takes a copy after the kernels.
@@ -381,13 +414,14 @@ int bad_id_check(const moe_desc *desc, const int32_t *host_status)
 }
 
 // moe_route_build's work (checks, launches, eager readback) for a handle
-// whose workspace is set.
+// whose workspace is set; pairs: the workspace takes the row list too.
 int route_build(const moe_desc *desc, const void *topk_idx, const float *topk_w,
                 float *multihot_probs, const moe_handle *handle, int32_t *host_status,
-                void *stream)
+                void *stream, bool pairs = true)
 {
     moe::RouteArgs a;
-    int rc = route_launch(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream, a);
+    int rc = route_launch(desc, topk_idx, topk_w, multihot_probs, handle, host_status, stream, a,
+                          pairs);
     if (rc == MOE_OK && desc->mode == MOE_EAGER) {
         if ((rc = route_wait(handle, host_status, stream, a)) == MOE_OK)
             rc = bad_id_check(desc, host_status);
@@ -462,7 +496,7 @@ int moe_route_build_noalloc(const moe_desc *desc, const void *topk_idx, const fl
         return fail(MOE_ERR_ARG, "moe_route_build_noalloc takes its scratch from the library's "
                                  "fixed array: handle.workspace must be NULL and "
                                  "workspace_bytes 0 (it would be ignored)");
-    const size_t need = ws_layout(desc).bytes;
+    const size_t need = ws_layout(desc, false).bytes;
     if (need > kNoallocScratchBytes)
         return fail(MOE_ERR_WORKSPACE, "this route needs %zu bytes of scratch, more than the "
                                        "library's fixed %zu-byte array: use moe_route_build "
@@ -474,7 +508,9 @@ int moe_route_build_noalloc(const moe_desc *desc, const void *topk_idx, const fl
     moe_handle h = *handle;
     h.workspace = ws;
     h.workspace_bytes = kNoallocScratchBytes;
-    return route_build(desc, topk_idx, topk_w, multihot_probs, &h, host_status, stream);
+    // the caller's handle has no workspace, so the calls after it walk tokens:
+    // the route writes no row list into the shared array
+    return route_build(desc, topk_idx, topk_w, multihot_probs, &h, host_status, stream, false);
 }
 
 int moe_route_dispatch(const moe_desc *desc, const void *topk_idx, const float *topk_w,
@@ -669,6 +705,7 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     a.E_total = desc->E;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
+    a.pairs = handle_pairs(desc, handle, a.pg);
     moe::row_shape(a);
     hipError_t e = moe::launch_move_rows(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)

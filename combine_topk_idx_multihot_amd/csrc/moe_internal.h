@@ -20,6 +20,36 @@ constexpr int kRowThreads = kRowWaves * kWave;
 // would need more (a row array past 64 GiB, for instance).
 constexpr int64_t kMaxRowBlocks = 0xFFFFFFFFll / kRowThreads;
 
+// A route whose count table has at most this many entries (blocks x local
+// experts) is finished by one pass of one workgroup per block.
+constexpr int64_t kFusedFinishMax = 65536;
+constexpr int kXcds = 8;  // MI355X: workgroup j runs on XCD j mod 8
+
+// The route's row list.  For layers whose local experts take most routes
+// (k * EL >= 2 E), the finishing pass also writes, into the handle's
+// workspace, the (row, token) of every data row in an order made for the
+// row kernels: tokens are cut into tiles of about 512 (whole route blocks),
+// tile tau belongs to XCD tau mod 8, and a tile's rows are listed in
+// address order (expert by expert, ascending token).  Entry i is consumed by
+// wave i % 4 of workgroup i / 4, which runs on XCD (i / 4) mod 8, so the
+// rows of a tile are written by one XCD one after another, in address order,
+// while the tile's token rows (about 512 x 2H bytes) stay in that XCD's L2
+// for their up to k reads.  Each tile has a fixed range of cap positions in
+// its XCD's sequence; positions past the tile's rows hold row -1.
+struct PairGeom {
+    int64_t bpt = 0;           // route blocks per tile
+    int64_t tile_tokens = 0;   // tokens per tile (the last tile may have fewer)
+    int64_t ntiles = 0;
+    int64_t tiles_per_xcd = 0;
+    int64_t kk = 0;            // min(k, EL): rows a token can have
+    int64_t cap = 0;           // positions per tile, tile_tokens * kk
+    int64_t entries = 0;       // kXcds * (tiles_per_xcd * cap rounded up to a multiple of 4)
+};
+// Whether the route of this description writes the row list: several route
+// blocks, the fused finishing pass, and dense routing.
+bool pairs_form(int64_t T, int k, int E, int EL, int tokens_per_block, int64_t nblk);
+PairGeom pair_geom(int64_t T, int k, int EL, int tokens_per_block, int64_t nblk);
+
 // Launch geometry of the routing-count kernel: one workgroup covers
 // tokens_per_block whole tokens (k slots each, one thread per slot).
 struct RouteGeom {
@@ -46,6 +76,8 @@ struct RouteArgs {
     int32_t tokens_per_block;
     int64_t nblk;
     int32_t idx_i64;
+    int2 *pairs = nullptr;   // the row list (workspace), or null: not written
+    PairGeom pg;
 };
 
 // K1 counts + multihot map + in-block ranks; K2 offsets and final rows.
@@ -78,6 +110,10 @@ struct RowArgs {
     int64_t ndot_blocks;       // combine backward with dw: periods of 4 tokens, 0 otherwise
     int32_t keep_tail = 0;     // eager, R = the buffers' capacity: rows past the total are
                                // left as they are (no sentinel fill)
+    const int2 *pairs = nullptr; // the route's row list: rows are walked from it, not by token
+    PairGeom pg;
+    int64_t npair_blocks = 0;  // workgroups walking the row list (4 entries each)
+    int64_t nzero_blocks = 0;  // combine backward from the list: dw of slots without a row
 };
 
 // Row movement: dispatch (x -> rows, or with rows_q set x -> E4M3 rows and

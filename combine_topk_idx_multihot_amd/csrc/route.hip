@@ -35,6 +35,10 @@
 #ifndef MOE_ROUTE_MAX_THREADS
 #define MOE_ROUTE_MAX_THREADS 512
 #endif
+// 0: no row list (the row kernels walk tokens), for measurement
+#ifndef MOE_ROW_LIST
+#define MOE_ROW_LIST 1
+#endif
 
 namespace moe {
 
@@ -45,7 +49,37 @@ constexpr int kExpertBits = 10;
 
 __device__ __forceinline__ int packed_expert(int v) { return (v >> kRankBits) & ((1 << kExpertBits) - 1); }
 __device__ __forceinline__ int packed_rank(int v) { return v & ((1 << kRankBits) - 1); }
-constexpr int64_t kFusedFinishMax = 65536;  // nblk * EL bound for the fused finish
+
+bool pairs_form(int64_t T, int k, int E, int EL, int tokens_per_block, int64_t nblk)
+{
+    (void)T;
+    (void)tokens_per_block;
+    return MOE_ROW_LIST && nblk > 1 && nblk * EL <= kFusedFinishMax &&
+           static_cast<int64_t>(k) * EL >= 2 * static_cast<int64_t>(E);
+}
+
+PairGeom pair_geom(int64_t T, int k, int EL, int tokens_per_block, int64_t nblk)
+{
+    PairGeom g;
+    // tiles of about 512 tokens (4 MB of token rows at H = 4096: one XCD's
+    // L2), and at least one tile per XCD while there are enough blocks
+    int64_t bpt = 512 / tokens_per_block;
+    if (bpt < 1)
+        bpt = 1;
+    if (nblk / kXcds >= 1 && bpt > nblk / kXcds)
+        bpt = nblk / kXcds;
+    if (nblk < kXcds)
+        bpt = 1;
+    g.bpt = bpt;
+    g.tile_tokens = bpt * tokens_per_block;
+    g.ntiles = T > 0 ? (T + g.tile_tokens - 1) / g.tile_tokens : 0;
+    g.tiles_per_xcd = (g.ntiles + kXcds - 1) / kXcds;
+    g.kk = k < EL ? k : EL;
+    g.cap = g.tile_tokens * g.kk;
+    // each XCD's sequence rounded up to whole workgroups (4 entries)
+    g.entries = kXcds * ((g.tiles_per_xcd * g.cap + 3) / 4 * 4);
+    return g;
+}
 
 RouteGeom route_geom(int64_t T, int k, int EL)
 {
@@ -319,6 +353,13 @@ __device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, i
 // ---------------------------------------------------------------------------
 // K2 (fused finish)
 // ---------------------------------------------------------------------------
+// Entry of position p of XCD x's sequence in the row list: workgroup
+// (p / 4) * 8 + x (which runs on XCD x), wave p % 4.
+__device__ __forceinline__ int64_t pair_index(int64_t p, int64_t x)
+{
+    return ((p >> 2) * kXcds + x) * 4 + (p & 3);
+}
+
 __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
 {
     __shared__ int32_t pall[1024];  // [G][EL] partial totals
@@ -326,10 +367,17 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     __shared__ int32_t tot[1024];   // per-expert totals
     __shared__ int32_t base[1024];  // this block's per-expert base
     __shared__ int32_t offl[1025];  // offsets
+    // row list: the tile's blocks before this one, and the tile's counts
+    __shared__ int32_t ptb[1024], ptc[1024]; // [G][EL] partial sums
+    __shared__ int32_t tbase[1024];          // per expert: this block's base within its tile
+    __shared__ int32_t tpref[1025];          // tile rows of the experts before, [EL] = tile rows
     const int tid = threadIdx.x;
     const int EL = a.EL;
     const int64_t nblk = a.nblk;
     const int64_t b = blockIdx.x;
+    const bool lists = a.pairs != nullptr;
+    const int64_t bt0 = lists ? (b / a.pg.bpt) * a.pg.bpt : 0; // the tile's first block
+    const int64_t bt1 = lists ? min(nblk, bt0 + a.pg.bpt) : 0;
 
     // this block's slots, fetched now so their latency overlaps the count reads
     const int64_t t0 = b * a.tokens_per_block;
@@ -354,35 +402,77 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
         const int64_t per = (nblk + G - 1) / G;
         const int64_t b0 = static_cast<int64_t>(g) * per;
         const int64_t b1 = min(nblk, b0 + per);
-        int all = 0, before = 0;
+        int all = 0, before = 0, tb = 0, tc = 0;
 #pragma unroll 8
         for (int64_t bb = b0; bb < b1; ++bb) {
             const int c = a.counts[bb * EL + e];
             all += c;
             before += bb < b ? c : 0;
+            tb += (bb >= bt0 && bb < b) ? c : 0;
+            tc += (bb >= bt0 && bb < bt1) ? c : 0;
         }
         pall[g * EL + e] = all;
         pbef[g * EL + e] = before;
+        ptb[g * EL + e] = tb;
+        ptc[g * EL + e] = tc;
     }
     __syncthreads();
     if (tid < EL) {
-        int tot_e = 0, base_e = 0;
+        int tot_e = 0, base_e = 0, tb_e = 0, tc_e = 0;
         for (int gg = 0; gg < G; ++gg) {
             tot_e += pall[gg * EL + tid];
             base_e += pbef[gg * EL + tid];
+            tb_e += ptb[gg * EL + tid];
+            tc_e += ptc[gg * EL + tid];
         }
         tot[tid] = tot_e;
         base[tid] = base_e;
+        tbase[tid] = tb_e;
+        ptc[tid] = tc_e; // the tile's count per expert
     }
     __syncthreads();
+    // the tile's rows in address order: exclusive scan of its per-expert
+    // counts (wave 1; publish's scan runs on wave 0, and its barrier covers both)
+    if (lists && tid >= kWave && tid < 2 * kWave) {
+        const int lane = tid - kWave;
+        const int per = (EL + kWave - 1) / kWave;
+        const int e0 = min(EL, lane * per);
+        const int e1 = min(EL, e0 + per);
+        int sc = 0;
+        for (int x = e0; x < e1; ++x)
+            sc += ptc[x];
+        const int incl = wave_incl_scan(sc, lane);
+        int run = incl - sc;
+        for (int x = e0; x < e1; ++x) {
+            tpref[x] = run;
+            run += ptc[x];
+        }
+        if (lane == kWave - 1)
+            tpref[EL] = incl;
+    }
     RouteArgs pa = a;
     if (b != 0)
         pa.status = nullptr; // only block 0 publishes
     publish(pa, tot, offl, flags);
 
+    const int64_t tau = lists ? b / a.pg.bpt : 0;                // this block's tile
+    const int64_t tile_pos = lists ? (tau / kXcds) * a.pg.cap : 0; // its first position
     if (tid < nslots && packed >= 0) {
         const int ex = packed_expert(packed);
-        a.row_of_slot[s] = offl[ex] + base[ex] + packed_rank(packed);
+        const int row = offl[ex] + base[ex] + packed_rank(packed);
+        a.row_of_slot[s] = row;
+        if (lists) {
+            // repeated ids write their first slot's entry again (same value)
+            const int64_t q = tpref[ex] + tbase[ex] + packed_rank(packed);
+            a.pairs[pair_index(tile_pos + q, tau % kXcds)] =
+                make_int2(row, static_cast<int>(t0 + tid / a.k));
+        }
+    }
+    if (lists && b == bt0) {
+        // the tile's positions past its rows are empty
+        const int64_t tt = min(a.pg.tile_tokens, a.T - tau * a.pg.tile_tokens);
+        for (int64_t q = tpref[EL] + tid; q < tt * a.pg.kk; q += 1024)
+            a.pairs[pair_index(tile_pos + q, tau % kXcds)] = make_int2(-1, -1);
     }
 }
 

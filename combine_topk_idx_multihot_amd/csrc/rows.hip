@@ -510,6 +510,225 @@ __global__ void __launch_bounds__(kRowThreads) k_move_rows(RowArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Rows walked from the route's row list (dense routing, a handle with its
+// workspace): one wave per data row, the list entries laid out so that the
+// rows of a token tile are written one after another, in address order, by
+// the XCD whose L2 holds the tile's token rows (their up to k reads hit it).
+// Measured on MI355X against the token-major walk, which writes each token's
+// row to its k scattered rows: the combine backward at T = 4096, H = 2048
+// 55-56 -> 47.5 us, at T = 16384, H = 4096 448 -> 403 us.
+// ---------------------------------------------------------------------------
+// The list entry of wave `wave` of list workgroup pb: (row, token), or row -1
+// for an empty position, a position past the last tile, or a row outside
+// [0, R).  Uniform over the wave.
+__device__ __forceinline__ int2 list_entry(const RowArgs &a, int64_t pb, int wave)
+{
+    // positions and tiles fit 32 bits (the list has at most T * k < 2^31 entries)
+    const int2 none = make_int2(-1, -1);
+    const int x = static_cast<int>(pb % kXcds);
+    const int p = static_cast<int>(pb / kXcds) * 4 + wave;
+    const int cap = static_cast<int>(a.pg.cap);
+    const int i = p / cap;
+    const int tau = x + kXcds * i;
+    if (tau >= a.pg.ntiles)
+        return none;
+    const int q = p - i * cap;
+    const int64_t t0 = static_cast<int64_t>(tau) * a.pg.tile_tokens;
+    const int64_t tt = min(a.pg.tile_tokens, a.T - t0);
+    if (q >= tt * a.pg.kk)
+        return none;
+    const int2 pr = a.pairs[pb * 4 + wave];
+    // a row past R, or a token outside the entry's tile, is no row: the
+    // accesses stay inside the buffers whatever the workspace holds
+    if (pr.x < 0 || pr.x >= a.R || pr.y < t0 || pr.y >= t0 + tt)
+        return none;
+    return make_int2(__builtin_amdgcn_readfirstlane(pr.x), __builtin_amdgcn_readfirstlane(pr.y));
+}
+
+constexpr int kListBatch = 4;  // 16-byte chunks per lane in flight (4 KiB of a row per wave)
+
+// One batch of a row: chunks c0 + i * 64 + lane, i < kListBatch.  FULL: every
+// chunk exists (no per-chunk test, so the loads issue back to back).
+template <bool FULL>
+__device__ __forceinline__ void list_copy_batch(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                int c0, int nch, int lane)
+{
+    u32x4 v[kListBatch];
+#pragma unroll
+    for (int i = 0; i < kListBatch; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (FULL || c < nch)
+            v[i] = src[c];
+    }
+#pragma unroll
+    for (int i = 0; i < kListBatch; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (FULL || c < nch)
+            put16<MOE_NT_COPY_ROWS != 0>(dst + c, v[i]);
+    }
+}
+
+// Dispatch of one row from the list: the token's row copied whole, its token
+// and merged weight recorded (the first slot's weight plus its repeats', in
+// slot order).
+__device__ __forceinline__ void list_dispatch(const RowArgs &a, int64_t pb)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int2 rt = list_entry(a, pb, wave);
+    const int r = rt.x, t = rt.y;
+    if (r < 0)
+        return;
+    // the token's slots and weights (for row_w), loaded now so that their
+    // latency overlaps the row's
+    const int k = a.k;
+    const int64_t s = static_cast<int64_t>(t) * k + lane;
+    const int rj = (a.row_w && lane < k) ? a.row_of_slot[s] : -1;
+    const float wj = (a.row_w && lane < k && a.topk_w) ? a.topk_w[s] : 0.f;
+    const int nch = a.H >> 3;
+    const u32x4 *__restrict__ src = reinterpret_cast<const u32x4 *>(a.src + static_cast<int64_t>(t) * a.H);
+    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + static_cast<int64_t>(r) * a.H);
+    constexpr int B = kListBatch * kWave;
+    const int nfull = nch / B * B;
+    for (int c0 = 0; c0 < nfull; c0 += B)
+        list_copy_batch<true>(src, dst, c0, nch, lane);
+    if (nfull < nch)
+        list_copy_batch<false>(src, dst, nfull, nch, lane);
+    if (a.row_token && lane == 0)
+        a.row_token[r] = t;
+    if (a.row_w) {
+        uint64_t m = __ballot(rj == r);
+        float W = 0.f;
+        bool first = true;
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
+            W = first ? v : W + v;
+            first = false;
+        }
+        if (lane == 0)
+            a.row_w[r] = W;
+    }
+}
+
+// One batch of the combine backward's row: grad_out's chunks copied to the
+// grad row and multiplied with the expert-output row's into the fp64 sum.
+template <bool FULL>
+__device__ __forceinline__ void list_bwd_batch(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                               const u32x4 *__restrict__ frow, int c0, int nch,
+                                               int lane, double &acc)
+{
+    u32x4 g[kListBatch], f[kListBatch];
+#pragma unroll
+    for (int i = 0; i < kListBatch; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (FULL || c < nch) {
+            g[i] = src[c];
+            f[i] = __builtin_nontemporal_load(frow + c);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kListBatch; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (FULL || c < nch) {
+            put16<MOE_NT_COPY_ROWS != 0>(dst + c, g[i]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = fma(static_cast<double>(bf16_lo(g[i][q])), static_cast<double>(bf16_lo(f[i][q])), acc);
+                acc = fma(static_cast<double>(bf16_hi(g[i][q])), static_cast<double>(bf16_hi(f[i][q])), acc);
+            }
+        }
+    }
+}
+
+// Combine backward of one row from the list (launched with dw; expert_out is
+// given whenever a row exists): grad_out's token row copied to the grad row,
+// and its dot with the
+// expert-output row (exact products, fp64 sums: each lane's elements in
+// order, then a fixed butterfly) given to every slot of the token that names
+// the row.
+__device__ __forceinline__ void list_bwd(const RowArgs &a, int64_t pb)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int2 rt = list_entry(a, pb, wave);
+    const int r = rt.x, t = rt.y;
+    if (r < 0)
+        return;
+    // the token's slots (for dw), loaded now so that their latency overlaps
+    // the rows'
+    const int k = a.k;
+    const int64_t s = static_cast<int64_t>(t) * k + lane;
+    const int rj = lane < k ? a.row_of_slot[s] : -1;
+    const int nch = a.H >> 3;
+    const u32x4 *__restrict__ src = reinterpret_cast<const u32x4 *>(a.src + static_cast<int64_t>(t) * a.H);
+    u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + static_cast<int64_t>(r) * a.H);
+    const u32x4 *__restrict__ frow = reinterpret_cast<const u32x4 *>(a.F + static_cast<int64_t>(r) * a.H);
+    constexpr int B = kListBatch * kWave;
+    const int nfull = nch / B * B;
+    double acc = 0.0;
+    for (int c0 = 0; c0 < nfull; c0 += B)
+        list_bwd_batch<true>(src, dst, frow, c0, nch, lane, acc);
+    if (nfull < nch)
+        list_bwd_batch<false>(src, dst, frow, nfull, nch, lane, acc);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1)
+        acc += __shfl_xor(acc, o);
+    if (rj == r)
+        a.dw[s] = static_cast<float>(acc);
+}
+
+// dw of the slots that have no row (empty, not local, or outside [0, R)):
+// one thread per slot.
+__device__ __forceinline__ void zero_dw_no_row(const RowArgs &a, int64_t zb)
+{
+    const int64_t s = zb * kRowThreads + threadIdx.x;
+    if (s >= a.T * a.k)
+        return;
+    const int r = a.row_of_slot[s];
+    if (r < 0 || r >= a.R)
+        a.dw[s] = 0.f;
+}
+
+// Grid: [sentinel blocks][list blocks][expert blocks].
+__global__ void __launch_bounds__(kRowThreads) k_rows_list(RowArgs a)
+{
+    int64_t bid = blockIdx.x;
+    if (bid < a.nsent_blocks) {
+        fill_sentinel(a, bid);
+        return;
+    }
+    bid -= a.nsent_blocks;
+    if (bid < a.npair_blocks) {
+        list_dispatch(a, bid);
+        return;
+    }
+    fill_expert(a, static_cast<int>(bid - a.npair_blocks));
+}
+
+// Grid: [sentinel blocks][list blocks][dw-zero blocks][expert blocks].
+__global__ void __launch_bounds__(kRowThreads) k_bwd_list(RowArgs a)
+{
+    int64_t bid = blockIdx.x;
+    if (bid < a.nsent_blocks) {
+        fill_sentinel(a, bid);
+        return;
+    }
+    bid -= a.nsent_blocks;
+    if (bid < a.npair_blocks) {
+        list_bwd(a, bid);
+        return;
+    }
+    bid -= a.npair_blocks;
+    if (bid < a.nzero_blocks) {
+        zero_dw_no_row(a, bid);
+        return;
+    }
+    fill_expert(a, static_cast<int>(bid - a.nzero_blocks));
+}
+
+// ---------------------------------------------------------------------------
 // Decode-sized route and dispatch in one launch.  A sync-free route of at
 // most kTinySlots slots (T*k <= 16) is cheap enough for every workgroup of
 // the dispatch to compute it from the ids into its own LDS, so no workgroup
@@ -1272,6 +1491,12 @@ void row_shape(RowArgs &a)
     a.ntok_blocks = (a.T + tpb - 1) / tpb;
     a.nexp_blocks = a.R > 0 ? a.EL : 0;
     a.nsent_blocks = sentinel_blocks(a);
+    // rows walked from the route's row list: the bf16 dispatch and the
+    // combine backward of a handle that carries one
+    if (a.rows_q)
+        a.pairs = nullptr;
+    a.npair_blocks = a.pairs ? a.pg.entries / 4 : 0;
+    a.nzero_blocks = (a.pairs && a.dw) ? (a.T * a.k + kRowThreads - 1) / kRowThreads : 0;
 }
 
 // The sync-free tail fill, a launch of its own.
@@ -1284,7 +1509,8 @@ bool move_rows_fits(const RowArgs &a)
 {
     // the sync-free tail's launch and the rows' launch, each within the limit
     return a.nsent_blocks <= kMaxRowBlocks &&
-           a.nsent_blocks + a.ntok_blocks + a.nexp_blocks + bwd_mid_blocks(a) <= kMaxRowBlocks;
+           a.nsent_blocks + a.ntok_blocks + a.nexp_blocks + bwd_mid_blocks(a) <= kMaxRowBlocks &&
+           a.nsent_blocks + a.npair_blocks + a.nzero_blocks + a.nexp_blocks <= kMaxRowBlocks;
 }
 
 hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
@@ -1296,6 +1522,17 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
         // sync-free: the tail first, on its own, then the rows
         launch(k_sentinel_oneshot, dim3(static_cast<unsigned>(a0.nsent_blocks)), dim3(kRowThreads), 0, s, a0);
         a.nsent_blocks = 0;
+    }
+    if (a.pairs) {
+        const int64_t nbl = a.nsent_blocks + a.npair_blocks + a.nzero_blocks + a.nexp_blocks;
+        if (nbl == 0)
+            return hipSuccess;
+        const dim3 gl(static_cast<unsigned>(nbl));
+        if (a.dw)
+            launch(k_bwd_list, gl, dim3(kRowThreads), 0, s, a);
+        else
+            launch(k_rows_list, gl, dim3(kRowThreads), 0, s, a);
+        return hipGetLastError();
     }
     const int64_t nmid = a.dw ? bwd_mid_blocks(a) : a.ntok_blocks;
     const int64_t nb = a.nsent_blocks + nmid + a.nexp_blocks;

@@ -107,8 +107,9 @@ typedef struct moe_handle {
                                    repeated ids point at the first slot's row */
     int32_t *status;            /* [4] {total, flags (MOE_FLAG_*), data rows, 0} */
     void *workspace;            /* >= moe_route_workspace_size(desc) bytes of device
-                                   scratch for moe_route_build (per-block counts);
-                                   read by no other call, which accept NULL */
+                                   memory: the route's scratch (per-block counts)
+                                   and, for dense routing, its row list (below);
+                                   the calls after the route accept NULL */
     size_t workspace_bytes;
 } moe_handle;
 
@@ -117,7 +118,23 @@ typedef struct moe_handle {
 int64_t moe_capacity_min(const moe_desc *desc);
 
 /* Device bytes of handle.workspace for this description (0 if the description
- * is invalid): about ceil(T*k/512) * (EL + 1) * 4 bytes. */
+ * is invalid): the route's scratch, about ceil(T/floor(B/k)) * (EL + 1) * 4
+ * bytes (route blocks of B = 512 slots up to 512 local experts, else 256),
+ * plus the row list when the route writes one.
+ *
+ * The row list: for dense routing the route also writes, into the workspace,
+ * every row's (row, token) pair, grouped by tiles of about 512 tokens and
+ * dealt over the GPU's 8 XCDs, rows of a tile in address order.
+ * moe_dispatch and moe_combine_bwd then walk that list instead of the tokens
+ * when the handle they get brings this workspace: each XCD's L2 holds its
+ * tiles' token rows while the expert rows stream past.  Results are the
+ * same either way.  The route writes the list when its T*k slots span more
+ * than one route block, (route blocks) * EL <= 65536, and k * EL >= 2 * E
+ * (under uniform routing a token then has two or more local slots); it
+ * takes about 8 * T * min(k, EL) bytes, rounded up to whole tiles on every
+ * XCD.  The list belongs to the handle: a route written through another
+ * handle that shares this workspace replaces it.  moe_route_build_noalloc
+ * writes no list (its handles have no workspace). */
 size_t moe_route_workspace_size(const moe_desc *desc);
 
 /*

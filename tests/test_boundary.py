@@ -124,8 +124,10 @@ def test_workspace_rules():
     need = B.moe_route_workspace_size(d)
     assert need > 0
     assert route_rc(d, ws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
-    # only route_build reads the workspace: dispatch gets past the handle check
-    # with none and stops at a later rule (weights with no row_w), launching nothing
+    # only route_build needs the workspace (dispatch reads the route's row list
+    # from it when it is there and walks tokens without it): dispatch gets past
+    # the handle check with none and stops at a later rule (weights with no
+    # row_w), launching nothing
     h = _handle(need - 1)
     h.workspace = None
     assert B.lib().moe_dispatch(ctypes.byref(d), ctypes.byref(h), FAKE, 2048, FAKE, 10, FAKE, None,
@@ -135,6 +137,35 @@ def test_workspace_rules():
     h.workspace = None
     assert route_rc(d, handle=h) == B.MOE_ERR_WORKSPACE
     assert B.lib().moe_route_workspace_size(ctypes.byref(_desc(k=0))) == 0
+
+
+def _up256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("T,E,k,EL", [
+    (4096, 128, 8, 128), (16384, 64, 8, 64), (1027, 16, 4, 16), (300, 8, 2, 8),
+    (64, 128, 8, 128), (65, 128, 8, 128), (4096, 128, 8, 16), (4096, 128, 8, 32),
+    (32768, 128, 8, 128), (32769, 128, 8, 128), (2100, 1024, 8, 1024), (1500, 8, 8, 2),
+    (999, 32, 6, 32), (40000, 64, 8, 64), (700, 64, 1, 64), (0, 8, 2, 8)])
+def test_workspace_size_follows_the_row_list_rule(T, E, k, EL):
+    """moe_route_workspace_size: the route's scratch (per-block counts and
+    flags), plus the row list exactly when the route spans several blocks,
+    the count table stays within 65536 entries and k * EL >= 2 * E; the list
+    is at least 8 bytes per (token, min(k, EL)) and at most that plus whole
+    tiles of 512 tokens on each of the 8 XCDs."""
+    d = _desc(T=T, E=E, k=k, num_local=EL, pad_multiple=1)
+    slots = 512 if EL <= 512 else 256
+    nblk = -(-T // (slots // k)) if T else 0
+    scratch = _up256(nblk * EL * 4) + _up256(nblk * 4)
+    got = B.moe_route_workspace_size(d)
+    listed = nblk > 1 and nblk * EL <= 65536 and k * EL >= 2 * E
+    if not listed:
+        assert got == max(scratch, 256)
+        return
+    kk = min(k, EL)
+    extra = got - scratch
+    assert 8 * T * kk <= extra <= _up256(8 * kk * (T + 8 * 512) + 8 * 8 * 3), (got, scratch)
 
 
 def test_noalloc_route_rules():
