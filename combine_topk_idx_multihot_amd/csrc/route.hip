@@ -39,6 +39,9 @@
 #ifndef MOE_ROW_LIST
 #define MOE_ROW_LIST 1
 #endif
+#ifndef MOE_LIST_TILE_TOKENS
+#define MOE_LIST_TILE_TOKENS 512
+#endif
 
 namespace moe {
 
@@ -61,15 +64,27 @@ bool pairs_form(int64_t T, int k, int E, int EL, int tokens_per_block, int64_t n
 PairGeom pair_geom(int64_t T, int k, int EL, int tokens_per_block, int64_t nblk)
 {
     PairGeom g;
-    // tiles of about 512 tokens (4 MB of token rows at H = 4096: one XCD's
-    // L2), and at least one tile per XCD while there are enough blocks
-    int64_t bpt = 512 / tokens_per_block;
-    if (bpt < 1)
-        bpt = 1;
-    if (nblk / kXcds >= 1 && bpt > nblk / kXcds)
-        bpt = nblk / kXcds;
-    if (nblk < kXcds)
-        bpt = 1;
+    // tiles of whole route blocks, at most about 512 tokens (4 MB of token
+    // rows at H = 4096: one XCD's L2; smaller tiles read the tokens fewer
+    // times but write shorter runs per expert and measure slower), tile t on
+    // XCD t mod 8.  The size is the largest whose busiest XCD walks at most
+    // 5 % more blocks than the best size's: 47 route blocks make 8 tiles of
+    // 6 (6 blocks on the busiest XCD) rather than 6 tiles of 8 (8), 94 make
+    // 16 of 6 (12) rather than 12 of 8 (16 on four XCDs, 8 on the others),
+    // and 625 make tiles of 8 (80) rather than of 1 (79).
+    int64_t most = MOE_LIST_TILE_TOKENS / tokens_per_block;
+    if (most < 1)
+        most = 1;
+    auto load = [&](int64_t b) { return b * (((nblk + b - 1) / b + kXcds - 1) / kXcds); };
+    int64_t least = load(1);
+    for (int64_t b = 2; b <= most; ++b)
+        least = load(b) < least ? load(b) : least;
+    int64_t bpt = 1;
+    for (int64_t b = most; b >= 1; --b)
+        if (load(b) * 20 <= least * 21) {
+            bpt = b;
+            break;
+        }
     g.bpt = bpt;
     g.tile_tokens = bpt * tokens_per_block;
     g.ntiles = T > 0 ? (T + g.tile_tokens - 1) / g.tile_tokens : 0;

@@ -545,27 +545,57 @@ __device__ __forceinline__ int2 list_entry(const RowArgs &a, int64_t pb, int wav
     return make_int2(__builtin_amdgcn_readfirstlane(pr.x), __builtin_amdgcn_readfirstlane(pr.y));
 }
 
-constexpr int kListBatch = 4;  // 16-byte chunks per lane in flight (4 KiB of a row per wave)
+// 16-byte chunks per lane that a wave of the list kernels loads before it
+// stores.  A wave's loads wait for its earlier stores too (one counter), so a
+// row moves best in one batch: the dispatch takes rows of up to 8 chunks per
+// lane (8 KiB, H = 4096) whole; the backward, which loads two rows (grad_out
+// and the expert output), up to 4 pairs.  Measured on MI355X at 16384 tokens,
+// H = 4096: dispatch 240 -> 222 us with 8 instead of 4; the backward is 2 %
+// slower with 8 pairs.
+constexpr int kListCopyMax = 8;
+constexpr int kListBwdMax = 4;
 
-// One batch of a row: chunks c0 + i * 64 + lane, i < kListBatch.  FULL: every
-// chunk exists (no per-chunk test, so the loads issue back to back).
-template <bool FULL>
-__device__ __forceinline__ void list_copy_batch(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                                int c0, int nch, int lane)
+// N chunks per lane, c0 + i * 64 + lane for i < N, all present: no per-chunk
+// test, so the loads issue back to back.
+template <int N>
+__device__ __forceinline__ void list_copy_n(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int c0,
+                                            int lane)
 {
-    u32x4 v[kListBatch];
+    u32x4 v[N];
 #pragma unroll
-    for (int i = 0; i < kListBatch; ++i) {
-        const int c = c0 + i * kWave + lane;
-        if (FULL || c < nch)
-            v[i] = src[c];
-    }
+    for (int i = 0; i < N; ++i)
+        v[i] = src[c0 + i * kWave + lane];
 #pragma unroll
-    for (int i = 0; i < kListBatch; ++i) {
-        const int c = c0 + i * kWave + lane;
-        if (FULL || c < nch)
-            put16<MOE_NT_COPY_ROWS != 0>(dst + c, v[i]);
-    }
+    for (int i = 0; i < N; ++i)
+        put16<MOE_NT_COPY_ROWS != 0>(dst + c0 + i * kWave + lane, v[i]);
+}
+
+// list_copy_n<n> for a wave-uniform n in [1, N].
+template <int N>
+__device__ __forceinline__ void list_copy_upto(int n, const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                               int c0, int lane)
+{
+    if (n == N)
+        list_copy_n<N>(src, dst, c0, lane);
+    else if constexpr (N > 1)
+        list_copy_upto<N - 1>(n, src, dst, c0, lane);
+}
+
+// A row of nch chunks (nch a multiple of 32): batches of kListCopyMax chunks
+// per lane, the rest in one batch of its own size, then the half-wave chunk
+// of an H that is an odd multiple of 256.
+__device__ __forceinline__ void list_copy_row(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int nch,
+                                              int lane)
+{
+    int n = nch / kWave;
+    int c0 = 0;
+    for (; n > kListCopyMax; n -= kListCopyMax, c0 += kListCopyMax * kWave)
+        list_copy_n<kListCopyMax>(src, dst, c0, lane);
+    if (n > 0)
+        list_copy_upto<kListCopyMax>(n, src, dst, c0, lane);
+    c0 += n * kWave;
+    if (c0 + lane < nch)
+        put16<MOE_NT_COPY_ROWS != 0>(dst + c0 + lane, src[c0 + lane]);
 }
 
 // Dispatch of one row from the list: the token's row copied whole, its token
@@ -588,12 +618,7 @@ __device__ __forceinline__ void list_dispatch(const RowArgs &a, int64_t pb)
     const int nch = a.H >> 3;
     const u32x4 *__restrict__ src = reinterpret_cast<const u32x4 *>(a.src + static_cast<int64_t>(t) * a.H);
     u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + static_cast<int64_t>(r) * a.H);
-    constexpr int B = kListBatch * kWave;
-    const int nfull = nch / B * B;
-    for (int c0 = 0; c0 < nfull; c0 += B)
-        list_copy_batch<true>(src, dst, c0, nch, lane);
-    if (nfull < nch)
-        list_copy_batch<false>(src, dst, nfull, nch, lane);
+    list_copy_row(src, dst, nch, lane);
     if (a.row_token && lane == 0)
         a.row_token[r] = t;
     if (a.row_w) {
@@ -612,34 +637,43 @@ __device__ __forceinline__ void list_dispatch(const RowArgs &a, int64_t pb)
     }
 }
 
-// One batch of the combine backward's row: grad_out's chunks copied to the
-// grad row and multiplied with the expert-output row's into the fp64 sum.
-template <bool FULL>
-__device__ __forceinline__ void list_bwd_batch(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                               const u32x4 *__restrict__ frow, int c0, int nch,
-                                               int lane, double &acc)
+// The combine backward's step on one 16-byte chunk: grad_out's chunk stored
+// to the grad row and multiplied with the expert output's into the fp64 sum.
+__device__ __forceinline__ void list_bwd_chunk(u32x4 *__restrict__ dst, const u32x4 &g, const u32x4 &f,
+                                               double &acc)
 {
-    u32x4 g[kListBatch], f[kListBatch];
+    put16<MOE_NT_COPY_ROWS != 0>(dst, g);
 #pragma unroll
-    for (int i = 0; i < kListBatch; ++i) {
-        const int c = c0 + i * kWave + lane;
-        if (FULL || c < nch) {
-            g[i] = src[c];
-            f[i] = __builtin_nontemporal_load(frow + c);
-        }
+    for (int q = 0; q < 4; ++q) {
+        acc = fma(static_cast<double>(bf16_lo(g[q])), static_cast<double>(bf16_lo(f[q])), acc);
+        acc = fma(static_cast<double>(bf16_hi(g[q])), static_cast<double>(bf16_hi(f[q])), acc);
+    }
+}
+
+// N chunk pairs per lane, all present, loads first (as list_copy_n).
+template <int N>
+__device__ __forceinline__ void list_bwd_n(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                           const u32x4 *__restrict__ frow, int c0, int lane, double &acc)
+{
+    u32x4 g[N], f[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        g[i] = src[c0 + i * kWave + lane];
+        f[i] = __builtin_nontemporal_load(frow + c0 + i * kWave + lane);
     }
 #pragma unroll
-    for (int i = 0; i < kListBatch; ++i) {
-        const int c = c0 + i * kWave + lane;
-        if (FULL || c < nch) {
-            put16<MOE_NT_COPY_ROWS != 0>(dst + c, g[i]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc = fma(static_cast<double>(bf16_lo(g[i][q])), static_cast<double>(bf16_lo(f[i][q])), acc);
-                acc = fma(static_cast<double>(bf16_hi(g[i][q])), static_cast<double>(bf16_hi(f[i][q])), acc);
-            }
-        }
-    }
+    for (int i = 0; i < N; ++i)
+        list_bwd_chunk(dst + c0 + i * kWave + lane, g[i], f[i], acc);
+}
+
+template <int N>
+__device__ __forceinline__ void list_bwd_upto(int n, const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                              const u32x4 *__restrict__ frow, int c0, int lane, double &acc)
+{
+    if (n == N)
+        list_bwd_n<N>(src, dst, frow, c0, lane, acc);
+    else if constexpr (N > 1)
+        list_bwd_upto<N - 1>(n, src, dst, frow, c0, lane, acc);
 }
 
 // Combine backward of one row from the list (launched with dw; expert_out is
@@ -665,13 +699,18 @@ __device__ __forceinline__ void list_bwd(const RowArgs &a, int64_t pb)
     const u32x4 *__restrict__ src = reinterpret_cast<const u32x4 *>(a.src + static_cast<int64_t>(t) * a.H);
     u32x4 *__restrict__ dst = reinterpret_cast<u32x4 *>(a.rows + static_cast<int64_t>(r) * a.H);
     const u32x4 *__restrict__ frow = reinterpret_cast<const u32x4 *>(a.F + static_cast<int64_t>(r) * a.H);
-    constexpr int B = kListBatch * kWave;
-    const int nfull = nch / B * B;
+    // each lane's chunks in ascending order: batches of kListBwdMax pairs,
+    // the rest in one batch, then the half-wave chunk (as list_copy_row)
     double acc = 0.0;
-    for (int c0 = 0; c0 < nfull; c0 += B)
-        list_bwd_batch<true>(src, dst, frow, c0, nch, lane, acc);
-    if (nfull < nch)
-        list_bwd_batch<false>(src, dst, frow, nfull, nch, lane, acc);
+    int n = nch / kWave;
+    int c0 = 0;
+    for (; n > kListBwdMax; n -= kListBwdMax, c0 += kListBwdMax * kWave)
+        list_bwd_n<kListBwdMax>(src, dst, frow, c0, lane, acc);
+    if (n > 0)
+        list_bwd_upto<kListBwdMax>(n, src, dst, frow, c0, lane, acc);
+    c0 += n * kWave;
+    if (c0 + lane < nch)
+        list_bwd_chunk(dst + c0 + lane, src[c0 + lane], __builtin_nontemporal_load(frow + c0 + lane), acc);
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1)
         acc += __shfl_xor(acc, o);
@@ -1505,6 +1544,38 @@ __global__ void __launch_bounds__(kRowThreads) k_sentinel_oneshot(RowArgs a)
     fill_sentinel_oneshot(a, blockIdx.x);
 }
 
+#ifndef MOE_LIST_FLIGHT_COPY
+#define MOE_LIST_FLIGHT_COPY 16384
+#endif
+#ifndef MOE_LIST_FLIGHT_BWD
+#define MOE_LIST_FLIGHT_BWD 24576
+#endif
+
+// Dynamic LDS that lets at most `waves` workgroups of kRowThreads threads
+// (one wave per SIMD each) reside on a CU at once (160 KiB of LDS per CU;
+// 512 bytes left for a kernel's own LDS); 0 = no cap.
+static size_t lds_cap(int waves)
+{
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    if (waves <= 0 || waves >= 8)
+        return 0;
+    return ((kLdsPerCu / waves) & ~static_cast<size_t>(511)) - 512;
+}
+
+// Waves per SIMD for a list kernel: about `flight` bytes of rows per SIMD in
+// flight, 2 to 8 waves.  Measured on MI355X (16384 and 4096 tokens, top-8,
+// all experts local): the list dispatch of 8 KiB rows (H = 4096) runs in
+// 245 us with 8 waves per SIMD, 219 us with 2 (16 KiB per SIMD); with 4 KiB
+// rows 4 waves are as fast as 8 or slightly faster.  The list backward
+// (two rows loaded per wave) 417 -> 405 us with 3 waves of 8 KiB rows,
+// best with 6 for 4 KiB rows (24 KiB).  The token-major kernels and the
+// tail fill lose at any cap (up to 2x at 2 waves), so they have none.
+static int list_waves(int32_t H, int64_t flight)
+{
+    const int64_t w = flight / (static_cast<int64_t>(H) * 2);
+    return static_cast<int>(w < 2 ? 2 : (w > 8 ? 8 : w));
+}
+
 bool move_rows_fits(const RowArgs &a)
 {
     // the sync-free tail's launch and the rows' launch, each within the limit
@@ -1529,9 +1600,10 @@ hipError_t launch_move_rows(const RowArgs &a0, hipStream_t s)
             return hipSuccess;
         const dim3 gl(static_cast<unsigned>(nbl));
         if (a.dw)
-            launch(k_bwd_list, gl, dim3(kRowThreads), 0, s, a);
+            launch(k_bwd_list, gl, dim3(kRowThreads), lds_cap(list_waves(a.H, MOE_LIST_FLIGHT_BWD)), s, a);
         else
-            launch(k_rows_list, gl, dim3(kRowThreads), 0, s, a);
+            launch(k_rows_list, gl, dim3(kRowThreads), lds_cap(list_waves(a.H, MOE_LIST_FLIGHT_COPY)), s,
+                   a);
         return hipGetLastError();
     }
     const int64_t nmid = a.dw ? bwd_mid_blocks(a) : a.ntok_blocks;

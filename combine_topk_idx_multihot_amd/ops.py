@@ -11,7 +11,7 @@ step runs in the HIP library:
 
   route(topk_idx, num_experts, local_begin, num_local, pad_multiple, capacity)
       -> (routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-          host_status)
+          workspace, host_status)
       capacity == 0 is the eager mode: host_status (CPU int32[4]) holds
       {total, flags, data rows, 0}, so R = host_status[0] with no further sync.
       capacity > 0 is the sync-free mode: R = capacity and nothing leaves the
@@ -28,8 +28,10 @@ step runs in the HIP library:
       backward: combine_bwd (moe_combine_bwd, the cached dispatch of grad_out)
 
 <handle tensors> = routing_map, tokens_per_expert, padded_offsets, row_of_slot,
-status, in that order.  The handle fields the ops need but do not carry (T, k,
-the number of local experts) are read off the tensors' shapes.
+status, workspace, in that order.  The workspace carries the route's row list
+(for dense routing), which the dispatch and the combine backward walk instead
+of the tokens.  The handle fields the ops need but do not carry (T, k, the
+number of local experts) are read off the tensors' shapes.
 
 ``moe_layer`` strings the ops together around a caller-supplied expert.
 """
@@ -48,12 +50,12 @@ def _desc(T, k, E, lb, EL, P, capacity, idx_i64=False):
     return B.make_desc(T, k, E, lb, EL, P, mode, idx_i64, capacity)
 
 
-def _rebuild(routing_map, tpe, off, ros, status, E, lb, P, capacity):
-    """The dispatch handle from its tensors (no workspace: only routing reads one)."""
+def _rebuild(routing_map, tpe, off, ros, status, workspace, E, lb, P, capacity):
+    """The dispatch handle from its tensors."""
     T, k = ros.shape
     desc = _desc(T, k, E, lb, tpe.numel(), P, capacity)
     h = B.Handle(desc=desc, routing_map=routing_map, tokens_per_expert=tpe, padded_offsets=off,
-                 row_of_slot=ros, status=status, host_status=_NO_HOST, workspace=None)
+                 row_of_slot=ros, status=status, host_status=_NO_HOST, workspace=workspace)
     return desc, h
 
 
@@ -64,7 +66,7 @@ def _rebuild(routing_map, tpe, off, ros, status, E, lb, P, capacity):
 def route(topk_idx: torch.Tensor, num_experts: int, local_begin: int, num_local: int,
           pad_multiple: int, capacity: int
           ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor,
-                     torch.Tensor]:
+                     torch.Tensor, torch.Tensor]:
     T, k = topk_idx.shape
     desc = _desc(T, k, num_experts, local_begin, num_local, pad_multiple, capacity,
                  topk_idx.dtype == torch.int64)
@@ -79,21 +81,26 @@ def route(topk_idx: torch.Tensor, num_experts: int, local_begin: int, num_local:
         status=torch.empty(4, dtype=torch.int32, device=dev),
         # eager: pinned, so the route kernel writes the count straight to the host
         host_status=torch.zeros(4, dtype=torch.int32, pin_memory=eager),
-        workspace=torch.empty(B.moe_route_workspace_size(desc), dtype=torch.uint8, device=dev))
+        # zeroed: the route leaves some of its bytes unwritten (never read by
+        # the kernels), and an op's outputs must not depend on stale memory
+        workspace=torch.zeros(B.moe_route_workspace_size(desc), dtype=torch.uint8, device=dev))
     B.moe_route_build(desc, topk_idx.contiguous(), h)
     return (h.routing_map, h.tokens_per_expert, h.padded_offsets, h.row_of_slot, h.status,
-            h.host_status)
+            h.workspace, h.host_status)
 
 
 @route.register_fake
 def _(topk_idx, num_experts, local_begin, num_local, pad_multiple, capacity):
     T, k = topk_idx.shape
     dev = topk_idx.device
+    desc = _desc(T, k, num_experts, local_begin, num_local, pad_multiple, capacity,
+                 topk_idx.dtype == torch.int64)
     return (topk_idx.new_empty((T, num_experts), dtype=torch.uint8),
             topk_idx.new_empty(num_local, dtype=torch.int32),
             topk_idx.new_empty(num_local + 1, dtype=torch.int32),
             topk_idx.new_empty((T, k), dtype=torch.int32),
             topk_idx.new_empty(4, dtype=torch.int32),
+            topk_idx.new_empty(B.moe_route_workspace_size(desc), dtype=torch.uint8),
             torch.empty(4, dtype=torch.int32, device="cpu") if dev.type != "cpu"
             else topk_idx.new_empty(4, dtype=torch.int32))
 
@@ -104,11 +111,11 @@ def _(topk_idx, num_experts, local_begin, num_local, pad_multiple, capacity):
 @torch.library.custom_op(f"{_NS}::dispatch", mutates_args=())
 def dispatch(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tensor,
              tokens_per_expert: torch.Tensor, padded_offsets: torch.Tensor,
-             row_of_slot: torch.Tensor, status: torch.Tensor, num_experts: int, local_begin: int,
-             pad_multiple: int, capacity: int, R: int
+             row_of_slot: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+             num_experts: int, local_begin: int, pad_multiple: int, capacity: int, R: int
              ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-                       num_experts, local_begin, pad_multiple, capacity)
+                       workspace, num_experts, local_begin, pad_multiple, capacity)
     H = x.shape[1]
     rows = x.new_empty((R, H))
     row_w = x.new_empty(R, dtype=torch.float32)
@@ -121,7 +128,7 @@ def dispatch(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tensor,
 
 @dispatch.register_fake
 def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-      num_experts, local_begin, pad_multiple, capacity, R):
+      workspace, num_experts, local_begin, pad_multiple, capacity, R):
     return (x.new_empty((R, x.shape[1])), x.new_empty(R, dtype=torch.float32),
             x.new_empty(R, dtype=torch.int32), x.new_empty(R, dtype=torch.int32))
 
@@ -129,13 +136,13 @@ def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, st
 @torch.library.custom_op(f"{_NS}::dispatch_fp8", mutates_args=())
 def dispatch_fp8(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tensor,
                  tokens_per_expert: torch.Tensor, padded_offsets: torch.Tensor,
-                 row_of_slot: torch.Tensor, status: torch.Tensor, num_experts: int,
-                 local_begin: int, pad_multiple: int, capacity: int, R: int
+                 row_of_slot: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+                 num_experts: int, local_begin: int, pad_multiple: int, capacity: int, R: int
                  ) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
     """FP8 dispatch: (rows_q [R,H] float8_e4m3fn, row_scale [R,H/128] fp32, row_w,
     row_token, row_expert).  Not differentiable (the codes are a quantization)."""
     desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-                       num_experts, local_begin, pad_multiple, capacity)
+                       workspace, num_experts, local_begin, pad_multiple, capacity)
     H = x.shape[1]
     rows_q = x.new_empty((R, H), dtype=torch.float8_e4m3fn)
     row_scale = x.new_empty((R, H // 128), dtype=torch.float32)
@@ -149,7 +156,7 @@ def dispatch_fp8(x: torch.Tensor, topk_w: torch.Tensor, routing_map: torch.Tenso
 
 @dispatch_fp8.register_fake
 def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-      num_experts, local_begin, pad_multiple, capacity, R):
+      workspace, num_experts, local_begin, pad_multiple, capacity, R):
     H = x.shape[1]
     return (x.new_empty((R, H), dtype=torch.float8_e4m3fn),
             x.new_empty((R, H // 128), dtype=torch.float32), x.new_empty(R, dtype=torch.float32),
@@ -159,11 +166,11 @@ def _(x, topk_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, st
 @torch.library.custom_op(f"{_NS}::dispatch_bwd", mutates_args=())
 def dispatch_bwd(grad_rows: torch.Tensor, grad_row_w: torch.Tensor, routing_map: torch.Tensor,
                  tokens_per_expert: torch.Tensor, padded_offsets: torch.Tensor,
-                 row_of_slot: torch.Tensor, status: torch.Tensor, num_experts: int,
-                 local_begin: int, pad_multiple: int, capacity: int
+                 row_of_slot: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+                 num_experts: int, local_begin: int, pad_multiple: int, capacity: int
                  ) -> tuple[torch.Tensor, torch.Tensor]:
     desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-                       num_experts, local_begin, pad_multiple, capacity)
+                       workspace, num_experts, local_begin, pad_multiple, capacity)
     R, H = grad_rows.shape
     T, k = row_of_slot.shape
     grad_x = grad_rows.new_empty((T, H))
@@ -175,28 +182,28 @@ def dispatch_bwd(grad_rows: torch.Tensor, grad_row_w: torch.Tensor, routing_map:
 
 @dispatch_bwd.register_fake
 def _(grad_rows, grad_row_w, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-      num_experts, local_begin, pad_multiple, capacity):
+      workspace, num_experts, local_begin, pad_multiple, capacity):
     T, k = row_of_slot.shape
     return (grad_rows.new_empty((T, grad_rows.shape[1])),
             grad_rows.new_empty((T, k), dtype=torch.float32))
 
 
 def _dispatch_setup(ctx, inputs, output):
-    x, _, routing_map, tpe, off, ros, status, E, lb, P, cap, R = inputs
-    ctx.save_for_backward(routing_map, tpe, off, ros, status)
+    x, _, routing_map, tpe, off, ros, status, ws, E, lb, P, cap, R = inputs
+    ctx.save_for_backward(routing_map, tpe, off, ros, status, ws)
     ctx.args = (E, lb, P, cap, R, x.shape[1], x.dtype)
 
 
 def _dispatch_backward(ctx, grad_rows, grad_row_w, _grad_token, _grad_expert):
-    routing_map, tpe, off, ros, status = ctx.saved_tensors
+    routing_map, tpe, off, ros, status, ws = ctx.saved_tensors
     E, lb, P, cap, R, H, dtype = ctx.args
     if grad_rows is None:
         grad_rows = ros.new_zeros((R, H), dtype=dtype)
     if grad_row_w is None:
         grad_row_w = ros.new_zeros(R, dtype=torch.float32)
     grad_x, grad_topk_w = dispatch_bwd(grad_rows, grad_row_w, routing_map, tpe, off, ros, status,
-                                       E, lb, P, cap)
-    return (grad_x, grad_topk_w) + (None,) * 10
+                                       ws, E, lb, P, cap)
+    return (grad_x, grad_topk_w) + (None,) * 11
 
 
 dispatch.register_autograd(_dispatch_backward, setup_context=_dispatch_setup)
@@ -208,9 +215,10 @@ dispatch.register_autograd(_dispatch_backward, setup_context=_dispatch_setup)
 @torch.library.custom_op(f"{_NS}::combine", mutates_args=())
 def combine(Y: torch.Tensor, routing_map: torch.Tensor, tokens_per_expert: torch.Tensor,
             padded_offsets: torch.Tensor, row_of_slot: torch.Tensor, status: torch.Tensor,
-            num_experts: int, local_begin: int, pad_multiple: int, capacity: int) -> torch.Tensor:
+            workspace: torch.Tensor, num_experts: int, local_begin: int, pad_multiple: int,
+            capacity: int) -> torch.Tensor:
     desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-                       num_experts, local_begin, pad_multiple, capacity)
+                       workspace, num_experts, local_begin, pad_multiple, capacity)
     R, H = Y.shape
     out = Y.new_empty((row_of_slot.shape[0], H))
     B.moe_combine(desc, h, Y.contiguous(), H, R, out)
@@ -218,18 +226,19 @@ def combine(Y: torch.Tensor, routing_map: torch.Tensor, tokens_per_expert: torch
 
 
 @combine.register_fake
-def _(Y, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status, num_experts,
-      local_begin, pad_multiple, capacity):
+def _(Y, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status, workspace,
+      num_experts, local_begin, pad_multiple, capacity):
     return Y.new_empty((row_of_slot.shape[0], Y.shape[1]))
 
 
 @torch.library.custom_op(f"{_NS}::combine_bwd", mutates_args=())
 def combine_bwd(grad_out: torch.Tensor, R: int, routing_map: torch.Tensor,
                 tokens_per_expert: torch.Tensor, padded_offsets: torch.Tensor,
-                row_of_slot: torch.Tensor, status: torch.Tensor, num_experts: int,
-                local_begin: int, pad_multiple: int, capacity: int) -> torch.Tensor:
+                row_of_slot: torch.Tensor, status: torch.Tensor, workspace: torch.Tensor,
+                num_experts: int, local_begin: int, pad_multiple: int, capacity: int
+                ) -> torch.Tensor:
     desc, h = _rebuild(routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-                       num_experts, local_begin, pad_multiple, capacity)
+                       workspace, num_experts, local_begin, pad_multiple, capacity)
     H = grad_out.shape[1]
     grad_rows = grad_out.new_empty((R, H))
     B.moe_combine_bwd(desc, h, grad_out.contiguous(), H, R, grad_rows)
@@ -238,21 +247,21 @@ def combine_bwd(grad_out: torch.Tensor, R: int, routing_map: torch.Tensor,
 
 @combine_bwd.register_fake
 def _(grad_out, R, routing_map, tokens_per_expert, padded_offsets, row_of_slot, status,
-      num_experts, local_begin, pad_multiple, capacity):
+      workspace, num_experts, local_begin, pad_multiple, capacity):
     return grad_out.new_empty((R, grad_out.shape[1]))
 
 
 def _combine_setup(ctx, inputs, output):
-    Y, routing_map, tpe, off, ros, status, E, lb, P, cap = inputs
-    ctx.save_for_backward(routing_map, tpe, off, ros, status)
+    Y, routing_map, tpe, off, ros, status, ws, E, lb, P, cap = inputs
+    ctx.save_for_backward(routing_map, tpe, off, ros, status, ws)
     ctx.args = (Y.shape[0], E, lb, P, cap)
 
 
 def _combine_backward(ctx, grad_out):
-    routing_map, tpe, off, ros, status = ctx.saved_tensors
+    routing_map, tpe, off, ros, status, ws = ctx.saved_tensors
     R, E, lb, P, cap = ctx.args
-    grad_rows = combine_bwd(grad_out, R, routing_map, tpe, off, ros, status, E, lb, P, cap)
-    return (grad_rows,) + (None,) * 9
+    grad_rows = combine_bwd(grad_out, R, routing_map, tpe, off, ros, status, ws, E, lb, P, cap)
+    return (grad_rows,) + (None,) * 10
 
 
 combine.register_autograd(_combine_backward, setup_context=_combine_setup)
@@ -270,11 +279,9 @@ def moe_layer(x, topk_idx, topk_w, experts, num_experts, local_begin=0, num_loca
     (R = capacity, pad and sentinel rows zero, capturable and traceable with
     static shapes); capacity == 0 reads the row count back once."""
     num_local = num_experts if num_local is None else num_local
-    rmap, tpe, off, ros, status, host = route(topk_idx, num_experts, local_begin, num_local,
-                                              pad_multiple, capacity)
+    *handle, host = route(topk_idx, num_experts, local_begin, num_local, pad_multiple, capacity)
     R = capacity if capacity > 0 else int(host[0])
-    rows, row_w, _, row_expert = dispatch(x, topk_w, rmap, tpe, off, ros, status, num_experts,
-                                          local_begin, pad_multiple, capacity, R)
+    rows, row_w, _, row_expert = dispatch(x, topk_w, *handle, num_experts, local_begin,
+                                          pad_multiple, capacity, R)
     Y = experts(rows, row_w, row_expert)
-    return combine(Y, rmap, tpe, off, ros, status, num_experts, local_begin, pad_multiple,
-                   capacity)
+    return combine(Y, *handle, num_experts, local_begin, pad_multiple, capacity)

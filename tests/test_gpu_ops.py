@@ -184,10 +184,10 @@ def test_opcheck():
     x, idx, w, _, _ = c.device_inputs()
     meta = ops.route(idx, c.E, c.lb, c.EL, c.P, c.C)
     torch.library.opcheck(ops.route, (idx, c.E, c.lb, c.EL, c.P, c.C))
-    args = (x, w) + tuple(meta[:5]) + (c.E, c.lb, c.P, c.C, c.C)
+    args = (x, w) + tuple(meta[:6]) + (c.E, c.lb, c.P, c.C, c.C)
     torch.library.opcheck(ops.dispatch, args)
     rows = ops.dispatch(*args)[0].detach().requires_grad_(True)
-    torch.library.opcheck(ops.combine, (rows,) + tuple(meta[:5]) + (c.E, c.lb, c.P, c.C))
+    torch.library.opcheck(ops.combine, (rows,) + tuple(meta[:6]) + (c.E, c.lb, c.P, c.C))
 
 
 def test_fp8_dispatch_op_matches_oracle():
@@ -195,7 +195,7 @@ def test_fp8_dispatch_op_matches_oracle():
     say("ops dispatch_fp8 (sync-free, H=768)")
     x, idx, w, _, _ = c.device_inputs()
     meta = ops.route(idx, c.E, c.lb, c.EL, c.P, c.C)
-    q, s, rw, rt, re = ops.dispatch_fp8(x.detach(), w.detach(), *meta[:5], c.E, c.lb, c.P, c.C,
+    q, s, rw, rt, re = ops.dispatch_fp8(x.detach(), w.detach(), *meta[:6], c.E, c.lb, c.P, c.C,
                                         c.C)
     torch.cuda.synchronize()
     ref = oracle.route(c.idx, c.E, c.lb, c.EL, c.P, sync_free=True, C=c.C, w=c.w)
@@ -205,5 +205,5 @@ def test_fp8_dispatch_op_matches_oracle():
     np.testing.assert_array_equal(rw.cpu().numpy().view(np.uint32), ref.row_w.view(np.uint32))
     np.testing.assert_array_equal(rt.cpu().numpy(), ref.row_token)
     np.testing.assert_array_equal(re.cpu().numpy(), ref.row_expert)
-    args = (x.detach(), w.detach()) + tuple(meta[:5]) + (c.E, c.lb, c.P, c.C, c.C)
+    args = (x.detach(), w.detach()) + tuple(meta[:6]) + (c.E, c.lb, c.P, c.C, c.C)
     torch.library.opcheck(ops.dispatch_fp8, args)

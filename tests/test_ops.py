@@ -4,6 +4,7 @@ import torch
 from torch._subclasses.fake_tensor import FakeTensorMode
 from torch.fx.experimental.proxy_tensor import make_fx
 
+from combine_topk_idx_multihot_amd import binding as B
 from combine_topk_idx_multihot_amd import ops
 
 OPS = ("route", "dispatch", "dispatch_fp8", "dispatch_bwd", "combine", "combine_bwd")
@@ -25,21 +26,24 @@ def test_fake_shapes():
         x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
         w = torch.empty((T, k), dtype=torch.float32, device="cuda")
         meta = ops.route(idx, E, 16, EL, P, C)
-        assert [tuple(t.shape) for t in meta] == [(T, E), (EL,), (EL + 1,), (T, k), (4,), (4,)]
-        assert meta[5].device.type == "cpu"
-        rows, row_w, rt, re = ops.dispatch(x, w, *meta[:5], E, 16, P, C, C)
+        desc = B.make_desc(T, k, E, 16, EL, P, B.MOE_SYNC_FREE, False, C)
+        ws = B.moe_route_workspace_size(desc)
+        assert [tuple(t.shape) for t in meta] == [(T, E), (EL,), (EL + 1,), (T, k), (4,), (ws,),
+                                                  (4,)]
+        assert meta[5].dtype == torch.uint8 and meta[6].device.type == "cpu"
+        rows, row_w, rt, re = ops.dispatch(x, w, *meta[:6], E, 16, P, C, C)
         assert rows.shape == (C, H) and rows.dtype == torch.bfloat16
         assert row_w.shape == rt.shape == re.shape == (C,)
         assert row_w.dtype == torch.float32 and rt.dtype == re.dtype == torch.int32
-        q, sc, qw, qt, qe = ops.dispatch_fp8(x, w, *meta[:5], E, 16, P, C, C)
+        q, sc, qw, qt, qe = ops.dispatch_fp8(x, w, *meta[:6], E, 16, P, C, C)
         assert q.shape == (C, H) and q.dtype == torch.float8_e4m3fn
         assert sc.shape == (C, H // 128) and sc.dtype == torch.float32
         assert qw.shape == qt.shape == qe.shape == (C,)
-        out = ops.combine(rows, *meta[:5], E, 16, P, C)
+        out = ops.combine(rows, *meta[:6], E, 16, P, C)
         assert out.shape == (T, H) and out.dtype == torch.bfloat16
-        gr = ops.combine_bwd(out, C, *meta[:5], E, 16, P, C)
+        gr = ops.combine_bwd(out, C, *meta[:6], E, 16, P, C)
         assert gr.shape == (C, H)
-        gx, gw = ops.dispatch_bwd(rows, row_w, *meta[:5], E, 16, P, C)
+        gx, gw = ops.dispatch_bwd(rows, row_w, *meta[:6], E, 16, P, C)
         assert gx.shape == (T, H) and gw.shape == (T, k) and gw.dtype == torch.float32
 
 
