@@ -375,6 +375,9 @@ __device__ __forceinline__ int64_t pair_index(int64_t p, int64_t x)
     return ((p >> 2) * kXcds + x) * 4 + (p & 3);
 }
 
+// LISTS: the route also writes the row list (a.pairs); the instance without
+// it keeps the shorter count loop (measured 1 us faster per route).
+template <bool LISTS>
 __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
 {
     __shared__ int32_t pall[1024];  // [G][EL] partial totals
@@ -382,15 +385,16 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
     __shared__ int32_t tot[1024];   // per-expert totals
     __shared__ int32_t base[1024];  // this block's per-expert base
     __shared__ int32_t offl[1025];  // offsets
-    // row list: the tile's blocks before this one, and the tile's counts
-    __shared__ int32_t ptb[1024], ptc[1024]; // [G][EL] partial sums
-    __shared__ int32_t tbase[1024];          // per expert: this block's base within its tile
-    __shared__ int32_t tpref[1025];          // tile rows of the experts before, [EL] = tile rows
+    // row list: [G][EL] partial sums of the tile's blocks before this one and
+    // of the whole tile, then per expert; the tile rows of the experts
+    // before, [EL] = tile rows
+    __shared__ int32_t ptb[LISTS ? 1024 : 1], ptc[LISTS ? 1024 : 1];
+    __shared__ int32_t tpref[LISTS ? 1025 : 1];
     const int tid = threadIdx.x;
     const int EL = a.EL;
     const int64_t nblk = a.nblk;
     const int64_t b = blockIdx.x;
-    const bool lists = a.pairs != nullptr;
+    constexpr bool lists = LISTS;
     const int64_t bt0 = lists ? (b / a.pg.bpt) * a.pg.bpt : 0; // the tile's first block
     const int64_t bt1 = lists ? min(nblk, bt0 + a.pg.bpt) : 0;
 
@@ -423,13 +427,17 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
             const int c = a.counts[bb * EL + e];
             all += c;
             before += bb < b ? c : 0;
-            tb += (bb >= bt0 && bb < b) ? c : 0;
-            tc += (bb >= bt0 && bb < bt1) ? c : 0;
+            if (lists) {
+                tb += (bb >= bt0 && bb < b) ? c : 0;
+                tc += (bb >= bt0 && bb < bt1) ? c : 0;
+            }
         }
         pall[g * EL + e] = all;
         pbef[g * EL + e] = before;
-        ptb[g * EL + e] = tb;
-        ptc[g * EL + e] = tc;
+        if (lists) {
+            ptb[g * EL + e] = tb;
+            ptc[g * EL + e] = tc;
+        }
     }
     __syncthreads();
     if (tid < EL) {
@@ -437,13 +445,18 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
         for (int gg = 0; gg < G; ++gg) {
             tot_e += pall[gg * EL + tid];
             base_e += pbef[gg * EL + tid];
-            tb_e += ptb[gg * EL + tid];
-            tc_e += ptc[gg * EL + tid];
+            if (lists) {
+                tb_e += ptb[gg * EL + tid];
+                tc_e += ptc[gg * EL + tid];
+            }
         }
         tot[tid] = tot_e;
         base[tid] = base_e;
-        tbase[tid] = tb_e;
-        ptc[tid] = tc_e; // the tile's count per expert
+        if (lists) {
+            // read back by this thread only, then the tile's scan below
+            ptb[tid] = tb_e; // per expert: this block's base within its tile
+            ptc[tid] = tc_e; // per expert: the tile's count
+        }
     }
     __syncthreads();
     // the tile's rows in address order: exclusive scan of its per-expert
@@ -478,7 +491,7 @@ __global__ void __launch_bounds__(1024) k_route_finish(RouteArgs a)
         a.row_of_slot[s] = row;
         if (lists) {
             // repeated ids write their first slot's entry again (same value)
-            const int64_t q = tpref[ex] + tbase[ex] + packed_rank(packed);
+            const int64_t q = tpref[ex] + ptb[ex] + packed_rank(packed);
             a.pairs[pair_index(tile_pos + q, tau % kXcds)] =
                 make_int2(row, static_cast<int>(t0 + tid / a.k));
         }
@@ -576,7 +589,10 @@ hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
     if (a.nblk == 1)
         return hipSuccess; // the counting pass finished the route (one workgroup)
     if (a.nblk > 0 && a.nblk * a.EL <= kFusedFinishMax) {
-        launch(k_route_finish, dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s, a);
+        if (a.pairs)
+            launch(k_route_finish<true>, dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s, a);
+        else
+            launch(k_route_finish<false>, dim3(static_cast<unsigned>(a.nblk)), dim3(1024), 0, s, a);
         return hipGetLastError();
     }
     launch(k_route_scan, dim3(1), dim3(1024), 0, s, a);

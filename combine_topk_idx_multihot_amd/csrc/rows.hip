@@ -1565,11 +1565,12 @@ static size_t lds_cap(int waves)
 // Waves per SIMD for a list kernel: about `flight` bytes of rows per SIMD in
 // flight, 2 to 8 waves.  Measured on MI355X (16384 and 4096 tokens, top-8,
 // all experts local): the list dispatch of 8 KiB rows (H = 4096) runs in
-// 245 us with 8 waves per SIMD, 219 us with 2 (16 KiB per SIMD); with 4 KiB
-// rows 4 waves are as fast as 8 or slightly faster.  The list backward
-// (two rows loaded per wave) 417 -> 405 us with 3 waves of 8 KiB rows,
-// best with 6 for 4 KiB rows (24 KiB).  The token-major kernels and the
-// tail fill lose at any cap (up to 2x at 2 waves), so they have none.
+// 245 us with 8 waves per SIMD, 219 us with 2 (16 KiB per SIMD) and 304 us
+// with 1; with 4 KiB rows 4 waves are as fast as 8 or slightly faster.  The
+// list backward (two rows loaded per wave) 417 -> 405 us with 3 waves of
+// 8 KiB rows (421 with 2), best with 6 for 4 KiB rows (24 KiB).  The
+// token-major kernels and the tail fill lose at any cap (up to 2x at 2
+// waves), so they have none.
 static int list_waves(int32_t H, int64_t flight)
 {
     const int64_t w = flight / (static_cast<int64_t>(H) * 2);
