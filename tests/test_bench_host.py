@@ -4,9 +4,14 @@ byte model held against the HBM traffic the hardware counters measured.
 profiles/traffic.json holds rocprofv3 FETCH_SIZE / WRITE_SIZE per launch of
 every call on the five measured layers, scaled by a plain copy of known size.
 The byte model counts each input once and each output once.  The row kernels
-re-read and over-write nothing, so the two must agree closely; a mistake in
-the model (a dropped metadata array, rows counted for the wrong R, the FP8
-scales forgotten) shows up as a mismatch of several percent.  The routing facts
+over-write nothing and, walking tokens, re-read nothing, so the two must agree
+closely; a mistake in the model (a dropped metadata array, rows counted for
+the wrong R, the FP8 scales forgotten) shows up as a mismatch of several
+percent.  The one known excess: a dispatch or combine backward that walks the
+route's row list keeps a tile of about 512 token rows in each XCD's L2 while
+it writes; at H = 4096 that tile (4 MB) is as large as the L2, and some token
+rows are fetched again (counted 1.13 and 1.10 times the model at 16384
+tokens; 2048-wide rows, a 2 MB tile, stay within 1 %).  The routing facts
 (data rows, padded rows, active tokens) come from the same seeded generators
 the benchmark uses.
 """
@@ -55,6 +60,13 @@ def model_bytes(wname, sets=4):
     return acc
 
 
+def walks_list(wl):
+    """The library's rule for writing the row list (see moe_route_workspace_size)."""
+    EL = wl.num_local
+    nblk = -(-wl.T // ((512 if EL <= 512 else 256) // wl.k))
+    return nblk > 1 and nblk * EL <= 65536 and wl.k * EL >= 2 * wl.E
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
@@ -70,16 +82,26 @@ def test_byte_model_matches_counted_traffic(wname):
     # counters see and the model does not): only a layer of well under a MB
     # per call, the tiny one, notices, hence the absolute slack.
     slack = 256 << 10
+    wl = inputs.WORKLOADS[wname]
+    lists = walks_list(wl)
+    token_bytes = wl.T * wl.H * 2
     for call in ROW_CALLS:
         diff = meas[call]["bytes"] - model[call]
         # the row kernels: within 2.5 % (measured 1.000 to 1.021 on the
-        # large layers)
-        assert abs(diff) <= max(0.025 * model[call], slack), (wname, call, diff / model[call])
+        # large layers) ...
+        lo = hi = max(0.025 * model[call], slack)
+        if lists and call in ("dispatch", "combine_bwd"):
+            # ... except token rows fetched again by the list walk: at most
+            # two more reads of the token matrix (measured 1.2 and 1.7)
+            hi = max(hi, 2 * token_bytes)
+        assert -lo <= diff <= hi, (wname, call, diff / model[call])
     # the route's two passes hand the packed slot ranks and the per-block
-    # counts through memory, which the model does not count: measured 1.10 to
-    # 1.24 times the model, a few MB at most
+    # counts through memory, and a dense route writes its row list (8 bytes
+    # per row), none of which the model counts: measured 1.10 to 1.24 times
+    # the model without the list, 1.36 to 1.41 with it, a few MB at most
     r = meas["route"]["bytes"] / model["route"]
-    assert 1.0 <= r and meas["route"]["bytes"] <= 1.3 * model["route"] + slack, (wname, r)
+    extra = 8 * wl.T * min(wl.k, wl.num_local) if lists else 0
+    assert 1.0 <= r and meas["route"]["bytes"] <= 1.3 * model["route"] + extra + slack, (wname, r)
 
 
 def test_traffic_is_null_once_sources_change(monkeypatch):
