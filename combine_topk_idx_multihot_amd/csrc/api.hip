@@ -338,6 +338,7 @@ moe::RouteGeom route_args(const moe_desc *desc, const void *topk_idx, const floa
     a.EL = desc->num_local;
     a.P = desc->pad_multiple;
     a.tokens_per_block = g.tokens_per_block;
+    a.slots = g.slots;
     a.nblk = g.nblk;
     a.idx_i64 = desc->idx_is_i64;
     a.host_status = nullptr;

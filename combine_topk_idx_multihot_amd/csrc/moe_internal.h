@@ -51,10 +51,11 @@ bool pairs_form(int64_t T, int k, int E, int EL, int tokens_per_block, int64_t n
 PairGeom pair_geom(int64_t T, int k, int EL, int tokens_per_block, int64_t nblk);
 
 // Launch geometry of the routing-count kernel: one workgroup covers
-// tokens_per_block whole tokens (k slots each, one thread per slot).
+// tokens_per_block whole tokens (k slots each, `slots` slots per thread).
 struct RouteGeom {
-    int threads;          // 1024, 512 or 256 (the LDS bitmaps hold EL x threads bits)
-    int tokens_per_block; // threads / k
+    int threads;          // 1024, 512 or 256 (the LDS bitmaps hold EL x threads x slots bits)
+    int slots;            // slots per thread: 1, or 2 for a one-workgroup route of up to 2048 slots
+    int tokens_per_block; // threads * slots / k
     int64_t nblk;         // ceil(T / tokens_per_block)
 };
 RouteGeom route_geom(int64_t T, int k, int EL);
@@ -74,6 +75,7 @@ struct RouteArgs {
     int64_t T;
     int32_t k, E, lb, EL, P;
     int32_t tokens_per_block;
+    int32_t slots = 1;     // slots per thread of the counting kernel (RouteGeom)
     int64_t nblk;
     int32_t idx_i64;
     int2 *pairs = nullptr;   // the row list (workspace), or null: not written

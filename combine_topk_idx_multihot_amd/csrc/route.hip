@@ -96,6 +96,8 @@ PairGeom pair_geom(int64_t T, int k, int EL, int tokens_per_block, int64_t nblk)
     return g;
 }
 
+constexpr int kOneBlockThreads = 1024;
+
 RouteGeom route_geom(int64_t T, int k, int EL)
 {
     RouteGeom g;
@@ -108,6 +110,25 @@ RouteGeom route_geom(int64_t T, int k, int EL)
         g.threads = MOE_ROUTE_MAX_THREADS;
     g.tokens_per_block = g.threads / k;
     g.nblk = T > 0 ? (T + g.tokens_per_block - 1) / g.tokens_per_block : 0;
+    g.slots = 1;
+    // A small route in one workgroup of 1024 threads, which publishes the
+    // route itself (no finishing pass): up to 1024 slots with at most 256
+    // local experts, or 2048 slots at 2 per thread with at most 64.  Measured
+    // on MI355X (top-8, 128 local experts, map and probs): 96 and 128 tokens
+    // 10.2 and 10.5 us (two passes) -> 8.0 and 8.5 us; but 256 tokens at 2
+    // slots per thread 10.8 -> 13.7 us, the scans over 64 bitmap words per
+    // expert costing more than the second pass; with 32 local experts the
+    // captured decode layer of 256 tokens gained 0.4-1.3 us.
+    if (g.nblk > 1) {
+        const int sp = (T <= kOneBlockThreads / k && EL <= 256) ? 1
+                     : (T <= 2 * kOneBlockThreads / k && EL <= 64) ? 2 : 0;
+        if (sp) {
+            g.threads = kOneBlockThreads;
+            g.slots = sp;
+            g.tokens_per_block = kOneBlockThreads * sp / k;
+            g.nblk = 1;
+        }
+    }
     return g;
 }
 
@@ -117,30 +138,34 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // K1
 // ---------------------------------------------------------------------------
-// LDS of K1: slot bitmaps [EL][W] u32 and their popcount prefixes [EL][W] u16
-// (W = threads/32 words per expert), staged ids and weights, one flag word.
-static size_t count_lds_bytes(int threads, int EL)
+// LDS of K1 for a block of `slots` slots: slot bitmaps [EL][W] u32 and their
+// popcount prefixes [EL][W] u16 (W = slots/32 words per expert), staged ids
+// and weights, one flag word.
+static size_t count_lds_bytes(int slots, int EL)
 {
-    const size_t words = static_cast<size_t>(EL) * (threads / 32);
+    const size_t words = static_cast<size_t>(EL) * (slots / 32);
     return words * 4 + ((words + 1) & ~static_cast<size_t>(1)) * 2 +
-           static_cast<size_t>(threads) * 8 + 4 +
+           static_cast<size_t>(slots) * 8 + 4 +
            (2 * static_cast<size_t>(EL) + 1) * 4; // totals and offsets (one-block routes)
 }
 
 __device__ void publish(const RouteArgs &a, const int32_t *tot, int32_t *offl, int flags);
 
-template <typename IT>
+// S slots per thread: slot j*blockDim + tid of the block for j < S (S > 1
+// only for a route in one workgroup of up to 2048 slots).
+template <typename IT, int S>
 __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
 {
     extern __shared__ int32_t lds[];
     const int nthreads = blockDim.x;
-    const int W = nthreads / 32; // bitmap words per expert
+    const int nsl = nthreads * S;  // slots of a full block
+    const int W = nsl / 32;        // bitmap words per expert (a divisor of 64)
     const int EL = a.EL;
     uint32_t *bm = reinterpret_cast<uint32_t *>(lds);          // [EL][W] slots of each expert
     uint16_t *pref = reinterpret_cast<uint16_t *>(bm + EL * W); // [EL][W] exclusive popcounts
     int32_t *sid = reinterpret_cast<int32_t *>(pref + ((EL * W + 1) & ~1)); // staged ids
-    float *sw = reinterpret_cast<float *>(sid + nthreads);                   // staged weights
-    int32_t *bflag = reinterpret_cast<int32_t *>(sw + nthreads);
+    float *sw = reinterpret_cast<float *>(sid + nsl);                        // staged weights
+    int32_t *bflag = reinterpret_cast<int32_t *>(sw + nsl);
     int32_t *tot = bflag + 1;  // [EL] the block's counts (one-block routes)
     int32_t *offl = tot + EL;  // [EL+1] offsets (one-block routes)
 
@@ -152,18 +177,23 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
     const int64_t t0 = b * a.tokens_per_block;
     const int64_t t1 = min(a.T, t0 + a.tokens_per_block);
     const int nslots = static_cast<int>((t1 - t0) * k);
-    const int64_t s = t0 * k + tid;
+    const int64_t s0 = t0 * k; // the block's first slot
 
     for (int i = tid; i < EL * W; i += nthreads)
         bm[i] = 0;
-    int myid = -1; // -2 marks an id outside [-1, E)
-    if (tid < nslots) {
-        const int64_t e = static_cast<int64_t>(idx[s]);
-        myid = (e >= -1 && e < a.E) ? static_cast<int>(e) : -2;
+    int myid[S]; // -2 marks an id outside [-1, E)
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int ls = j * nthreads + tid;
+        myid[j] = -1;
+        if (ls < nslots) {
+            const int64_t e = static_cast<int64_t>(idx[s0 + ls]);
+            myid[j] = (e >= -1 && e < a.E) ? static_cast<int>(e) : -2;
+        }
+        sid[ls] = myid[j];
+        if (a.probs)
+            sw[ls] = ls < nslots ? a.w[s0 + ls] : 0.f;
     }
-    sid[tid] = myid;
-    if (a.probs)
-        sw[tid] = tid < nslots ? a.w[s] : 0.f;
     if (tid == 0)
         *bflag = 0;
     // Zero this block's rows of the map and the probs (coalesced); the routed
@@ -196,42 +226,57 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
 
     // One thread per slot: a repeated id points back at its first slot; the
     // first slot of a local expert sets its bit in that expert's bitmap.
-    const bool bad = myid == -2;
-    bool dup = false;
-    int prim_back = 0, tl = 0, j = 0;
-    if (myid >= 0) {
-        tl = tid / k;
-        j = tid - tl * k;
-        for (int q = 0; q < j; ++q) {
-            if (sid[tl * k + q] == myid) {
-                dup = true;
-                prim_back = j - q;
-                break;
+    bool dup[S];
+    int prim_back[S], tl[S], jt[S], ep[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int ls = j * nthreads + tid;
+        const int id = myid[j];
+        const bool bad = id == -2;
+        dup[j] = false;
+        prim_back[j] = 0;
+        tl[j] = 0;
+        jt[j] = 0;
+        if (id >= 0) {
+            tl[j] = ls / k;
+            jt[j] = ls - tl[j] * k;
+            for (int q = 0; q < jt[j]; ++q) {
+                if (sid[tl[j] * k + q] == id) {
+                    dup[j] = true;
+                    prim_back[j] = jt[j] - q;
+                    break;
+                }
             }
         }
+        ep[j] = (id >= a.lb && id < a.lb + EL) ? id - a.lb : -1;
+        if (id >= 0 && !dup[j]) {
+            if (ep[j] >= 0)
+                atomicOr(&bm[ep[j] * W + (ls >> 5)], 1u << (ls & 31));
+            if (a.map)
+                a.map[(t0 + tl[j]) * a.E + id] = 1;
+        }
+        const uint64_t mbad = __ballot(bad);
+        const uint64_t mdup = __ballot(dup[j]);
+        if (lane == 0 && (mbad | mdup))
+            atomicOr(bflag, (mbad ? 1 : 0) | (mdup ? 2 : 0));
     }
-    const int ep = (myid >= a.lb && myid < a.lb + EL) ? myid - a.lb : -1;
-    if (myid >= 0 && !dup) {
-        if (ep >= 0)
-            atomicOr(&bm[ep * W + (tid >> 5)], 1u << (tid & 31));
-        if (a.map)
-            a.map[(t0 + tl) * a.E + myid] = 1;
-    }
-    const uint64_t mbad = __ballot(bad);
-    const uint64_t mdup = __ballot(dup);
-    if (lane == 0 && (mbad | mdup))
-        atomicOr(bflag, (mbad ? 1 : 0) | (mdup ? 2 : 0));
     __syncthreads();
 
     const int bf = *bflag;
-    if (a.probs && myid >= 0 && !dup) {
-        // the first slot's weight plus later repeats of the id, in slot order
-        float wt = sw[tid];
-        if (bf & 2)
-            for (int q = j + 1; q < k; ++q)
-                if (sid[tl * k + q] == myid)
-                    wt = wt + sw[tl * k + q];
-        a.probs[(t0 + tl) * a.E + myid] = wt;
+    if (a.probs) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            if (myid[j] < 0 || dup[j])
+                continue;
+            // the first slot's weight plus later repeats of the id, in slot order
+            const int ls = j * nthreads + tid;
+            float wt = sw[ls];
+            if (bf & 2)
+                for (int q = jt[j] + 1; q < k; ++q)
+                    if (sid[tl[j] * k + q] == myid[j])
+                        wt = wt + sw[tl[j] * k + q];
+            a.probs[(t0 + tl[j]) * a.E + myid[j]] = wt;
+        }
     }
     // Exclusive popcount prefix of each expert's bitmap; the total is the
     // block's count for that expert.  W consecutive lanes take one expert's W
@@ -240,7 +285,7 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
         const int c = __popc(bm[i]);
         int incl = c;
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
+        for (int o = 1; o < kWave; o <<= 1) {
             if (o < W) {
                 const int n = __shfl_up(incl, o, W);
                 if ((lane & (W - 1)) >= o)
@@ -257,34 +302,27 @@ __global__ void __launch_bounds__(1024) k_route_count(RouteArgs a)
         a.blockflags[b] = bf;
     __syncthreads();
 
-    if (a.nblk == 1) {
-        // The whole route is this workgroup: its counts are the totals, so it
-        // publishes the offsets and the status itself and writes final rows;
-        // no finishing pass is launched.
-        publish(a, tot, offl, bf);
-        if (tid < nslots) {
-            int v = -1;
-            if (ep >= 0) {
-                const int p = tid - prim_back;
-                const int w = p >> 5;
-                v = offl[ep] + pref[ep * W + w] + __popc(bm[ep * W + w] & ((1u << (p & 31)) - 1u));
-            }
-            a.row_of_slot[s] = v;
-        }
-        return;
-    }
-
     // In-block rank = earlier slots of the same expert = prefix + popcount of
     // the bits below the owning slot (the first slot, for a repeated id).
-    if (tid < nslots) {
+    // The whole route in this workgroup: its counts are the totals, so it
+    // publishes the offsets and the status itself and writes final rows; no
+    // finishing pass is launched.
+    const bool one = a.nblk == 1;
+    if (one)
+        publish(a, tot, offl, bf);
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int ls = j * nthreads + tid;
+        if (ls >= nslots)
+            continue;
         int v = -1;
-        if (ep >= 0) {
-            const int p = tid - prim_back;
+        if (ep[j] >= 0) {
+            const int p = ls - prim_back[j];
             const int w = p >> 5;
-            const int r = pref[ep * W + w] + __popc(bm[ep * W + w] & ((1u << (p & 31)) - 1u));
-            v = (ep << kRankBits) | r;
+            const int r = pref[ep[j] * W + w] + __popc(bm[ep[j] * W + w] & ((1u << (p & 31)) - 1u));
+            v = one ? offl[ep[j]] + r : (ep[j] << kRankBits) | r;
         }
-        a.row_of_slot[s] = v;
+        a.row_of_slot[s0 + ls] = v;
     }
 }
 
@@ -578,11 +616,19 @@ hipError_t launch_route(const RouteArgs &a, int threads, hipStream_t s)
 {
     hipError_t err;
     if (a.nblk > 0) {
-        const size_t lds = count_lds_bytes(threads, a.EL);
-        if (a.idx_i64)
-            launch(k_route_count<int64_t>, dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s, a);
-        else
-            launch(k_route_count<int32_t>, dim3(static_cast<unsigned>(a.nblk)), dim3(threads), lds, s, a);
+        const size_t lds = count_lds_bytes(threads * a.slots, a.EL);
+        const dim3 g(static_cast<unsigned>(a.nblk)), blk(threads);
+        if (a.slots == 2) {
+            if (a.idx_i64)
+                launch(k_route_count<int64_t, 2>, g, blk, lds, s, a);
+            else
+                launch(k_route_count<int32_t, 2>, g, blk, lds, s, a);
+        } else {
+            if (a.idx_i64)
+                launch(k_route_count<int64_t, 1>, g, blk, lds, s, a);
+            else
+                launch(k_route_count<int32_t, 1>, g, blk, lds, s, a);
+        }
         if ((err = hipGetLastError()) != hipSuccess)
             return err;
     }

@@ -119,8 +119,9 @@ int64_t moe_capacity_min(const moe_desc *desc);
 
 /* Device bytes of handle.workspace for this description (0 if the description
  * is invalid): the route's scratch, about ceil(T/floor(B/k)) * (EL + 1) * 4
- * bytes (route blocks of B = 512 slots up to 512 local experts, else 256),
- * plus the row list when the route writes one.
+ * bytes (route blocks of B = 512 slots up to 512 local experts, else 256; a
+ * route of T <= floor(1024/k) tokens with EL <= 256, or T <= floor(2048/k)
+ * with EL <= 64, is one block), plus the row list when the route writes one.
  *
  * The row list: for dense routing the route also writes, into the workspace,
  * every row's (row, token) pair, grouped by tiles of about 512 tokens and
@@ -128,8 +129,8 @@ int64_t moe_capacity_min(const moe_desc *desc);
  * moe_dispatch and moe_combine_bwd then walk that list instead of the tokens
  * when the handle they get brings this workspace: each XCD's L2 holds its
  * tiles' token rows while the expert rows stream past.  Results are the
- * same either way.  The route writes the list when its T*k slots span more
- * than one route block, (route blocks) * EL <= 65536, and k * EL >= 2 * E
+ * same either way.  The route writes the list when it takes more than one
+ * route block, (route blocks) * EL <= 65536, and k * EL >= 2 * E
  * (under uniform routing a token then has two or more local slots); it
  * takes about 8 * T * min(k, EL) bytes, rounded up to whole tiles on every
  * XCD.  The list belongs to the handle: a route written through another

@@ -60,10 +60,23 @@ def model_bytes(wname, sets=4):
     return acc
 
 
+def route_blocks(T, k, EL):
+    """The library's count of route blocks: blocks of 512 slots up to 512
+    local experts (else 256), or one block of up to 2048 slots when its
+    local experts are few (T <= 1024 // k with EL <= 256, or T <= 2048 // k
+    with EL <= 64)."""
+    if T == 0:
+        return 0
+    nblk = -(-T // ((512 if EL <= 512 else 256) // k))
+    if nblk > 1 and (T <= 1024 // k and EL <= 256 or T <= 2048 // k and EL <= 64):
+        return 1
+    return nblk
+
+
 def walks_list(wl):
     """The library's rule for writing the row list (see moe_route_workspace_size)."""
     EL = wl.num_local
-    nblk = -(-wl.T // ((512 if EL <= 512 else 256) // wl.k))
+    nblk = route_blocks(wl.T, wl.k, EL)
     return nblk > 1 and nblk * EL <= 65536 and wl.k * EL >= 2 * wl.E
 
 

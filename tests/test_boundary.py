@@ -139,6 +139,19 @@ def test_workspace_rules():
     assert B.lib().moe_route_workspace_size(ctypes.byref(_desc(k=0))) == 0
 
 
+def route_blocks(T, k, EL):
+    """The library's count of route blocks: blocks of 512 slots up to 512
+    local experts (else 256), or one block of up to 2048 slots when its
+    local experts are few (T <= 1024 // k with EL <= 256, or T <= 2048 // k
+    with EL <= 64)."""
+    if T == 0:
+        return 0
+    nblk = -(-T // ((512 if EL <= 512 else 256) // k))
+    if nblk > 1 and (T <= 1024 // k and EL <= 256 or T <= 2048 // k and EL <= 64):
+        return 1
+    return nblk
+
+
 def _up256(n):
     return (n + 255) // 256 * 256
 
@@ -155,8 +168,7 @@ def test_workspace_size_follows_the_row_list_rule(T, E, k, EL):
     is at least 8 bytes per (token, min(k, EL)) and at most that plus whole
     tiles of 512 tokens on each of the 8 XCDs."""
     d = _desc(T=T, E=E, k=k, num_local=EL, pad_multiple=1)
-    slots = 512 if EL <= 512 else 256
-    nblk = -(-T // (slots // k)) if T else 0
+    nblk = route_blocks(T, k, EL)
     scratch = _up256(nblk * EL * 4) + _up256(nblk * 4)
     got = B.moe_route_workspace_size(d)
     listed = nblk > 1 and nblk * EL <= 65536 and k * EL >= 2 * E

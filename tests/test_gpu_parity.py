@@ -231,10 +231,22 @@ EDGE = [
     ("max_local_sync_free", 300, 1500, 6, 400, 1024, 2, True, 512, 0.05, False, False),
     ("max_k_64", 200, 100, 64, 10, 80, 2, False, 256, 0.05, False, False),
     ("max_k_64_sync_free", 100, 64, 64, 0, 64, 1, True, 256, 0.0, False, False),
-    # the route in one counting workgroup (512 slots at k = 8; 256 with more
-    # than 512 local experts) and one token past it
+    # the route in one counting workgroup: 512 slots at k = 8 (256 with more
+    # than 512 local experts); up to 1024 slots in one 1024-thread workgroup
+    # (EL <= 256), up to 2048 with 2 slots per thread (EL <= 64); one token
+    # past each limit, and the expert limits on either side
     ("one_route_block", 64, 128, 8, 0, 128, 16, False, 512, 0.05, False, False),
-    ("two_route_blocks", 65, 128, 8, 0, 128, 16, False, 512, 0.05, False, False),
+    ("one_block_65_tokens", 65, 128, 8, 0, 128, 16, False, 512, 0.05, False, False),
+    ("one_block_1024_slots", 128, 128, 8, 0, 128, 4, False, 256, 0.05, True, False),
+    ("one_block_2048_slots", 256, 128, 8, 0, 64, 16, False, 512, 0.05, True, True),
+    ("one_block_2048_slots_sync_free", 256, 128, 8, 0, 32, 1, True, 256, 0.1, True, False),
+    ("one_block_k6_341_tokens", 341, 64, 6, 0, 64, 3, True, 256, 0.1, True, False),
+    ("blocks_k6_342_tokens", 342, 64, 6, 0, 64, 3, True, 256, 0.1, True, False),
+    ("blocks_257_tokens", 257, 128, 8, 0, 128, 16, False, 256, 0.05, False, False),
+    ("one_block_256_local", 128, 512, 8, 0, 256, 2, False, 256, 0.05, False, False),
+    ("blocks_257_local", 128, 512, 8, 0, 257, 2, False, 256, 0.05, False, False),
+    ("one_block_64_local_2048_slots", 256, 256, 8, 0, 64, 2, True, 256, 0.05, True, False),
+    ("blocks_65_local_2048_slots", 256, 256, 8, 0, 65, 2, True, 256, 0.05, True, False),
     ("one_route_block_sync_free", 64, 128, 8, 0, 32, 1, True, 512, 0.0, False, False),
     ("one_route_block_1024_local", 32, 1024, 8, 0, 1024, 2, True, 256, 0.05, True, False),
     ("two_route_blocks_1024_local", 33, 1024, 8, 0, 1024, 2, False, 256, 0.05, False, True),

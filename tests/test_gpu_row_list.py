@@ -42,8 +42,8 @@ CASES = [
     ("k_gt_EL", 1500, 8, 8, 3, 2, 2, False, 256, 0.05, True, False),
     ("fewer_blocks_than_xcds", 300, 16, 8, 0, 16, 4, True, 512, 0.05, False, False),
     ("half_the_experts_local", 2048, 64, 8, 16, 32, 1, False, 2304, 0.0, False, False),
-    ("wide_rows", 600, 8, 2, 0, 8, 1, False, 9216, 0.0, False, False),
-    ("no_data_row", 600, 8, 2, 0, 8, 4, False, 256, 1.0, False, False),
+    ("wide_rows", 1200, 8, 2, 0, 8, 1, False, 9216, 0.0, False, False),
+    ("no_data_row", 1200, 8, 2, 0, 8, 4, False, 256, 1.0, False, False),
 ]
 
 
@@ -52,9 +52,16 @@ def _up256(n):
 
 
 def route_blocks(T, k, EL):
-    """Route blocks of 512 slots up to 512 local experts, else 256."""
-    per = (512 if EL <= 512 else 256) // k
-    return -(-T // per) if T else 0
+    """The library's count of route blocks: blocks of 512 slots up to 512
+    local experts (else 256), or one block of up to 2048 slots when its
+    local experts are few (T <= 1024 // k with EL <= 256, or T <= 2048 // k
+    with EL <= 64)."""
+    if T == 0:
+        return 0
+    nblk = -(-T // ((512 if EL <= 512 else 256) // k))
+    if nblk > 1 and (T <= 1024 // k and EL <= 256 or T <= 2048 // k and EL <= 64):
+        return 1
+    return nblk
 
 
 def list_offset(T, k, EL):
