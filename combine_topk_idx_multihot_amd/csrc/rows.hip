@@ -577,12 +577,12 @@ __device__ __forceinline__ int2 list_entry(const RowArgs &a, int64_t pb, int wav
 }
 
 // 16-byte chunks per lane that a wave of the list kernels loads before it
-// stores.  A wave's loads wait for its earlier stores too (one counter), so a
-// row moves best in one batch: the dispatch takes rows of up to 8 chunks per
-// lane (8 KiB, H = 4096) whole; the backward, which loads two rows (grad_out
-// and the expert output), up to 4 pairs.  Measured on MI355X at 16384 tokens,
-// H = 4096: dispatch 240 -> 222 us with 8 instead of 4; the backward is 2 %
-// slower with 8 pairs.
+// stores: the dispatch takes rows of up to 8 chunks per lane (8 KiB,
+// H = 4096) in one batch, the backward, which loads two rows (grad_out and
+// the expert output), up to 4 pairs.  A wave's loads also wait for its
+// earlier stores (one counter), so one batch per row keeps the row's loads
+// together; how many rows are in flight is set by the residency
+// (list_waves).  The backward measured 2 % slower with batches of 8 pairs.
 constexpr int kListCopyMax = 8;
 constexpr int kListBwdMax = 4;
 
@@ -709,10 +709,9 @@ __device__ __forceinline__ void list_bwd_upto(int n, const u32x4 *__restrict__ s
 
 // Combine backward of one row from the list (launched with dw; expert_out is
 // given whenever a row exists): grad_out's token row copied to the grad row,
-// and its dot with the
-// expert-output row (exact products, fp64 sums: each lane's elements in
-// order, then a fixed butterfly) given to every slot of the token that names
-// the row.
+// and its dot with the expert-output row (exact products, fp64 sums: each
+// lane's elements in order, then a fixed butterfly) given to every slot of
+// the token that names the row.
 __device__ __forceinline__ void list_bwd(const RowArgs &a, int64_t pb)
 {
     const int lane = threadIdx.x & (kWave - 1);
