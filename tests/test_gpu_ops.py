@@ -46,7 +46,10 @@ def from_bits(a):
 
 
 class Case:
-    def __init__(self, T=300, k=4, E=24, lb=4, EL=16, P=4, H=512, seed=0, sync_free=False,
+    # the default shape routes in 5 blocks with the local experts taking most
+    # slots (k * EL >= 2E), so the route writes its row list and the dispatch
+    # and the combine backward walk it, also under graph capture and compile
+    def __init__(self, T=640, k=4, E=24, lb=4, EL=16, P=4, H=512, seed=0, sync_free=False,
                  empty=False):
         rng = np.random.default_rng(seed)
         self.T, self.k, self.E, self.lb, self.EL, self.P, self.H = T, k, E, lb, EL, P, H

@@ -13,7 +13,10 @@ workspace, one without):
   - a list with two tokens exchanged moves exactly those two rows, so the
     list is what the dispatch follows when the handle brings it;
   - moe_route_dispatch over the list: eager rows past the total are left as
-    they were, sync-free rows equal the token walk's.
+    they were, sync-free rows equal the token walk's;
+  - the sync-free route, the list dispatch and the list combine backward
+    captured in one HIP graph and replayed on new inputs, with eager work in
+    between, equal the same calls run eagerly.
 The cases cover tiles on every XCD and fewer route blocks than XCDs, a ragged
 last tile, padding, sync-free sentinel rows, repeated and out-of-range ids,
 k > EL, a local share of the experts, rows whose length is not a whole number
@@ -231,3 +234,70 @@ def test_route_dispatch_over_the_list(sync_free):
     assert (rt[R:].cpu().numpy() == -9).all() and (re[R:].cpu().numpy() == -9).all()
     ref = oracle.route(idx, E, lb, EL, P, sync_free=sync_free, C=C, w=w, x=x)
     np.testing.assert_array_equal(rows_np[:R], ref.rows)
+
+
+def test_list_walks_replay_from_a_graph():
+    """Sync-free route (writing the list) + dispatch + combine backward with dw
+    captured in one HIP graph; each replay, on ids, tokens and gradients copied
+    into the captured buffers, equals an eager run of the same calls (also
+    with the list) on the same inputs."""
+    T, E, k, EL, P, H = 2048, 64, 8, 64, 4, 512
+    assert has_list(T, E, k, EL)
+    C = oracle.capacity_min(T, k, EL, P)
+    d = B.make_desc(T, k, E, 0, EL, P, B.MOE_SYNC_FREE, False, C)
+    say(f"[row list] graph replays T={T} E={E} k={k} EL={EL} P={P} H={H} C={C}")
+
+    def inputs_(seed):
+        r = np.random.default_rng(seed)
+        return (inputs.random_routing(T, E, k, r, p_invalid=0.05, allow_dup=True).astype(np.int32),
+                r.random((T, k), dtype=np.float32), inputs.bf16_normal((T, H), r),
+                inputs.bf16_normal((T, H), r), inputs.bf16_normal((C, H), r))
+
+    idx0, w0, x0, g0, F0 = inputs_(1)
+    idx_t, w_t = torch.from_numpy(idx0).cuda(), torch.from_numpy(w0).cuda()
+    x_t, g_t, F_t = to_dev_bf16(x0), to_dev_bf16(g0), to_dev_bf16(F0)
+    h = B.alloc_handle(d)
+    rows = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
+    row_w = torch.empty(C, dtype=torch.float32, device="cuda")
+    rt = torch.empty(C, dtype=torch.int32, device="cuda")
+    re = torch.empty(C, dtype=torch.int32, device="cuda")
+    gr = torch.empty((C, H), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step():
+        B.moe_route_build(d, idx_t, h, stream=stream)
+        B.moe_dispatch(d, h, x_t, H, C, rows, w_t, row_w, rt, re, stream=stream)
+        B.moe_combine_bwd(d, h, g_t, H, C, gr, F_t, dw, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for seed in (2, 3, 4):
+        idx, w, x, g, F = inputs_(seed)
+        idx_t.copy_(torch.from_numpy(idx))
+        w_t.copy_(torch.from_numpy(w))
+        x_t.copy_(to_dev_bf16(x))
+        g_t.copy_(to_dev_bf16(g))
+        F_t.copy_(to_dev_bf16(F))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (to_np_u16(rows), row_w.cpu().numpy().view(np.uint32), rt.cpu().numpy(),
+               re.cpu().numpy(), to_np_u16(gr), dw.cpu().numpy().view(np.uint32))
+        # the same calls eagerly on fresh outputs (eager work between replays)
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize()
+        want = (to_np_u16(rows), row_w.cpu().numpy().view(np.uint32), rt.cpu().numpy(),
+                re.cpu().numpy(), to_np_u16(gr), dw.cpu().numpy().view(np.uint32))
+        for name, a_, b_ in zip(("rows", "row_w", "row_token", "row_expert", "grad_rows", "dw"),
+                                got, want):
+            np.testing.assert_array_equal(a_, b_, err_msg=f"replay seed {seed}: {name}")
+        ref = oracle.route(idx, E, 0, EL, P, sync_free=True, C=C, w=w, x=x)
+        np.testing.assert_array_equal(got[0], ref.rows)
+        np.testing.assert_array_equal(got[2], ref.row_token)
