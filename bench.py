@@ -328,7 +328,10 @@ def measure(name, args, with_next, torch, B, inputs, ceil):
                    "rows": int(np.mean([f["R"] for f in facts])), "buffer_sets": args.sets},
         "us_per_layer": {"forward_device": round(kern["route"]["avg_us"] + kern["dispatch"]["avg_us"] + kern["combine"]["avg_us"], 2),
                          "backward_device": kern["combine_bwd"]["avg_us"],
-                         "step_wall": round(ms_per_step * 1e3, 2), "step_device": round(dev_us, 2)},
+                         "step_wall": round(ms_per_step * 1e3, 2), "step_device": round(dev_us, 2),
+                         # the metric's pair: dispatch + combine, their algorithmic bytes
+                         # over their summed device time
+                         "dispatch_combine": dispatch_combine(kern)},
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),
@@ -538,6 +541,15 @@ def decode_graph(torch, B, inputs, reps=100, layers=(1, 4, 16)):
                              **{f"L{L}_us_per_layer": v for L, v in per.items()}}
         del lay
     return out
+
+
+def dispatch_combine(kern):
+    """Dispatch + combine of one layer: summed device time (breakdown pass),
+    their algorithmic bytes over it, and the fraction of the HBM peak."""
+    us = kern["dispatch"]["avg_us"] + kern["combine"]["avg_us"]
+    nbytes = kern["dispatch"]["alg_bytes"] + kern["combine"]["alg_bytes"]
+    gbs = nbytes / (us * 1e-6) / 1e9 if us > 0 else 0.0
+    return {"us": round(us, 2), "GBps": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4)}
 
 
 def _events_ms(torch, stream, fn, reps):

@@ -117,6 +117,15 @@ def test_byte_model_matches_counted_traffic(wname):
     assert 1.0 <= r and meas["route"]["bytes"] <= 1.3 * model["route"] + extra + slack, (wname, r)
 
 
+def test_dispatch_combine_pair():
+    """us_per_layer.dispatch_combine: the two calls' algorithmic bytes over
+    their summed device time, as a fraction of the 8 TB/s peak."""
+    k = {"dispatch": {"avg_us": 200.0, "alg_bytes": 1.2e9},
+         "combine": {"avg_us": 200.0, "alg_bytes": 1.2e9}}
+    r = bench.dispatch_combine(k)
+    assert r == {"us": 400.0, "GBps": 6000.0, "frac": 0.75}
+
+
 def test_traffic_is_null_once_sources_change(monkeypatch):
     t = traffic()
     w = next(iter(t["workloads"]))
