@@ -7,9 +7,10 @@ and then runs both walks along the same handle tensors (one handle with the
 workspace, one without):
   - the list holds each data row's (row, token) pair exactly once and no
     other pair (the workspace is filled with -1 before the route);
-  - rows, row weights, row tokens and experts, and grad rows agree bit for
-    bit between the walks and with the oracle; dw of both walks meets the
-    oracle's bar (exact products, fp64 sums, one rounding);
+  - rows, row weights, row tokens and experts, and grad rows (with and
+    without dw) agree bit for bit between the walks and with the oracle; dw
+    of both walks meets the oracle's bar (exact products, fp64 sums, one
+    rounding);
   - a list with two tokens exchanged moves exactly those two rows, so the
     list is what the dispatch follows when the handle brings it;
   - moe_route_dispatch over the list: eager rows past the total are left as
@@ -161,6 +162,12 @@ def test_list_walk_matches_token_walk_and_oracle(case):
     np.testing.assert_array_equal(by_list["grad_rows"], gr)
     for res in (by_list, by_token):
         check_dw(res["dw"], dw, idx, ref.row_of_slot, g, F, lb, EL, E)
+    # the combine backward without expert outputs (grad rows only, no dw)
+    for hh in (h, token_walk(h)):
+        gr_only, no_dw = B.combine_bwd(d, hh, g_t, R)
+        torch.cuda.synchronize()
+        assert no_dw is None
+        np.testing.assert_array_equal(to_np_u16(gr_only), gr)
 
 
 def test_dispatch_follows_the_list():
