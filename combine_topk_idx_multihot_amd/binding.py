@@ -180,8 +180,9 @@ class Handle:
     row_of_slot: torch.Tensor          # [T,k] int32
     status: torch.Tensor               # [4] int32 (device)
     host_status: torch.Tensor          # [4] int32 (pinned host)
-    workspace: torch.Tensor | None     # [moe_route_workspace_size] uint8 (device); only
-                                       # moe_route_build reads it
+    workspace: torch.Tensor | None     # [moe_route_workspace_size] uint8 (device): the
+                                       # route's scratch and, for dense routing, its row
+                                       # list, which dispatch and combine_bwd walk
 
     def c(self) -> _Handle:
         """The C struct, checked and built once: a Handle's tensors are not to
