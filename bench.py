@@ -295,6 +295,11 @@ def measure(name, args, with_next, torch, B, inputs, ceil):
                                 for i in range(args.steps)]))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom_all = np.array([t.elapsed_ms() for t in dev_]) * 1e3
+    # whole steps back to back on the device: dominant-call start to the next
+    # step's, in (up to) 5 contiguous windows, and the median of the windows
+    per_step = np.array([dev_[i + 1].since_ms(dev_[i]) for i in range(args.steps - 1)]) * 1e3
+    windows = ([float(np.mean(w)) for w in np.array_split(per_step, min(5, len(per_step)))]
+               if len(per_step) else [])
     dom_ms = float(np.mean(dom_all)) * 1e-3
     dom_bytes = float(np.mean([facts[i % len(sets)][dominant] for i in range(args.steps)]))
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
@@ -331,7 +336,10 @@ def measure(name, args, with_next, torch, B, inputs, ceil):
                          "step_wall": round(ms_per_step * 1e3, 2), "step_device": round(dev_us, 2),
                          # the metric's pair: dispatch + combine, their algorithmic bytes
                          # over their summed device time
-                         "dispatch_combine": dispatch_combine(kern)},
+                         "dispatch_combine": dispatch_combine(kern),
+                         "step_windows": {"us_per_step": [round(w, 2) for w in windows],
+                                          "median_us_per_step": round(float(np.median(windows)), 2)
+                                          if windows else None}},
         "kernels": kern,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),

@@ -579,6 +579,15 @@ class KernelTimer:
                   "hipEventElapsedTime")
         return f.value
 
+    def since_ms(self, earlier: "KernelTimer") -> float:
+        """Device time from the start of `earlier`'s timed call to the start
+        of this one's (both done): for the same call in consecutive steps,
+        the device time of one whole step."""
+        f = ctypes.c_float()
+        self._hip(self._L.hipEventElapsedTime(ctypes.byref(f), earlier.start, self.start),
+                  "hipEventElapsedTime")
+        return f.value
+
     def close(self):
         for name in ("start", "stop"):
             e = self.__dict__.pop(name, None)
