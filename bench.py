@@ -42,6 +42,9 @@ MI355X's 8 TB/s, and against ceilings measured in the same run:
     store order and reading nothing (a token-major scatter of the data rows,
     plus a one-shot fill of the sync-free zero tail);
   * `hip_copy_GBps`: the HIP runtime's own 1 GiB device copy (torch copy_).
+The combine also carries `gather_read_us` / `gather_us`: a plain reference
+gather of the same rows along the same handle, reading only, then also writing
+the summed rows; `frac_of_gather(_read)` = that time / the combine's.
 `cpu_baseline` times the oracle on the host on a bounded sample of the same
 workload.  `next` times, outside the step, the FP8 dispatch and the dispatch
 backward on the same routings.  The metric is quoted at 4096 and at 16384
@@ -313,6 +316,13 @@ def measure(name, args, with_next, torch, B, inputs, ceil):
     for n in ("dispatch", "combine_bwd"):  # both write the layer's rows token-major
         kern[n]["write_bound_us"] = wb
         kern[n]["frac_of_write_bound"] = round(wb / kern[n]["avg_us"], 4)
+    # the combine against the reference gather of its rows: read only, and
+    # with the summed rows written
+    g_read, g_write = gather_bounds(sets, facts, args.steps, torch)
+    kern["combine"]["gather_read_us"] = g_read
+    kern["combine"]["gather_us"] = g_write
+    kern["combine"]["frac_of_gather"] = round(g_write / kern["combine"]["avg_us"], 4)
+    kern["combine"]["frac_of_gather_read"] = round(g_read / kern["combine"]["avg_us"], 4)
 
     result = {
         "metric": METRIC,
@@ -623,6 +633,31 @@ def write_bounds(wl, sets, facts, steps, torch, dense):
 
     one(0)
     return round(_events_ms(torch, stream, one, steps) * 1e3, 2)
+
+
+def gather_bounds(sets, facts, steps, torch):
+    """us per layer for the reference gather of the combine's rows along each
+    set's handle (the combine's segment size and load batches): read only,
+    then with the summed rows written to the set's output.  Rotates over the
+    sets like the step; average over `steps` calls."""
+    from combine_topk_idx_multihot_amd import ceiling as C
+
+    H = sets[0]["Y"].shape[1]
+    seg = 1 if H < 1024 else 2  # the combine's segment (KiB)
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1, dtype=torch.int32, device=sets[0]["Y"].device)
+
+    def run(i, write):
+        st = sets[i % len(sets)]
+        R = facts[i % len(sets)]["R"]
+        C.gather(st["h"].row_of_slot, st["Y"][:R], st["out"] if write else None,
+                 None if write else sink, seg_kib=seg)
+
+    run(0, False)
+    r = _events_ms(torch, stream, lambda i: run(i, False), steps)
+    run(0, True)
+    w = _events_ms(torch, stream, lambda i: run(i, True), steps)
+    return round(r * 1e3, 2), round(w * 1e3, 2)
 
 
 def oracle_steps(wl, a, budget_s, max_reps=500):

@@ -14,7 +14,8 @@ from . import binding as _B
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmoe_ceiling.so")
 
 # Every symbol include/moe_ceiling.h declares.
-EXPORTS = ("moe_ceiling_fill", "moe_ceiling_copy", "moe_ceiling_scatter", "moe_ceiling_xcd_map")
+EXPORTS = ("moe_ceiling_fill", "moe_ceiling_copy", "moe_ceiling_scatter", "moe_ceiling_gather",
+           "moe_ceiling_xcd_map")
 OK, ERR_ARG, ERR_HIP = 0, 1, 2
 
 _lib = None
@@ -31,6 +32,7 @@ def lib() -> ctypes.CDLL:
         L.moe_ceiling_fill.argtypes = [vp, sz, c, vp]
         L.moe_ceiling_copy.argtypes = [vp, vp, sz, c, vp]
         L.moe_ceiling_scatter.argtypes = [vp, i64, i32, i64, i32, vp, c, vp]
+        L.moe_ceiling_gather.argtypes = [vp, i64, i32, i64, i32, vp, vp, vp, c, vp]
         L.moe_ceiling_xcd_map.argtypes = [vp, i32, vp]
         for n in EXPORTS:
             getattr(L, n).restype = c
@@ -75,6 +77,26 @@ def scatter(row_of_slot: torch.Tensor, rows: torch.Tensor, seg_kib: int = 1, str
     _check(lib().moe_ceiling_scatter(_buf(row_of_slot, "row_of_slot"), T, k, R, H,
                                      _buf(rows, "rows"), seg_kib, _B._stream(stream)),
            "moe_ceiling_scatter")
+
+
+def gather(row_of_slot: torch.Tensor, Y: torch.Tensor, out: torch.Tensor | None = None,
+           sink: torch.Tensor | None = None, seg_kib: int = 2, stream=None):
+    """The combine's reads: each token's rows of Y [R,H] bf16 that
+    row_of_slot [T,k] int32 names, summed in fp32; the sums stored into out
+    [T,H] bf16 (truncated), or, with out None, nothing stored (read only; sink
+    is a one-word int32 GPU tensor)."""
+    if row_of_slot.dtype != torch.int32 or row_of_slot.dim() != 2 or Y.dim() != 2:
+        raise ValueError("row_of_slot must be [T,k] int32 and Y [R,H]")
+    T, k = row_of_slot.shape
+    R, H = Y.shape
+    if out is not None and (out.dim() != 2 or out.shape[0] < T or out.shape[1] != H):
+        raise ValueError("out must be [T,H]")
+    if out is None and (sink is None or sink.numel() < 1):
+        raise ValueError("a read-only gather needs a sink word")
+    _check(lib().moe_ceiling_gather(_buf(row_of_slot, "row_of_slot"), T, k, R, H, _buf(Y, "Y"),
+                                    None if out is None else _buf(out, "out"),
+                                    None if sink is None else _buf(sink, "sink"), seg_kib,
+                                    _B._stream(stream)), "moe_ceiling_gather")
 
 
 def xcd_map(nblocks: int = 4096, stream=None) -> torch.Tensor:

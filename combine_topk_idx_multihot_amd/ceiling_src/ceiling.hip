@@ -14,6 +14,11 @@
 //            segments of seg_kib KiB to every row the token's slots name,
 //            exactly the destinations (and the order of destinations in
 //            flight) of the dispatch's row stores, with no source reads.
+//   gather   the combine's reads: one wave per (token, segment), the
+//            segments of the token's named rows loaded (non-temporal) in
+//            batches of four before any is added, summed in fp32; with an output
+//            the summed segment is stored (truncated to bf16), without one
+//            nothing is (a read-only gather).
 //   xcd_map  the accelerator complex die (XCD) each workgroup of a grid ran
 //            on, read from the wave's XCC_ID hardware register: the row
 //            kernels number their workgroups on the assumption that
@@ -94,6 +99,98 @@ __global__ void __launch_bounds__(kWave *kWaves) k_scatter(const int32_t *__rest
             }
         }
     }
+}
+
+// One wave per (token, segment of SEG chunks per lane).  FULL: every chunk
+// of the segment exists (no per-chunk test).  out NULL: read only; the sink
+// word is written only when a sum has the all-ones NaN pattern, which finite
+// rows never give (it keeps the loads).
+template <int SEG, bool FULL>
+__global__ void __launch_bounds__(kWave *kWaves) k_gather(const int32_t *__restrict__ row_of_slot,
+                                                          int64_t T, int k, int64_t R, int nch,
+                                                          const u32x4 *__restrict__ Y,
+                                                          u32x4 *__restrict__ out,
+                                                          uint32_t *__restrict__ sink)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int SPAN = SEG * kWave;
+    const int nseg = (nch + SPAN - 1) / SPAN;
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x / kWave);
+    const int64_t t = gw / nseg;
+    if (t >= T)
+        return;
+    const int c0 = static_cast<int>(gw - t * nseg) * SPAN;
+    const int myrow = lane < k ? row_of_slot[t * k + lane] : -1;
+    float acc[SEG][8];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.f;
+    // the named rows only, in slot order, four at a time
+    uint64_t m = __ballot(myrow >= 0 && myrow < R);
+    while (m) {
+        int r[4];
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            r[u] = -1;
+            if (m) {
+                r[u] = __builtin_amdgcn_readlane(myrow, __builtin_ctzll(m));
+                m &= m - 1;
+                n = u + 1;
+            }
+        }
+        u32x4 f[4][SEG];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 *src = Y + static_cast<int64_t>(u < n ? r[u] : 0) * nch;
+#pragma unroll
+            for (int i = 0; i < SEG; ++i) {
+                const int c = c0 + i * kWave + lane;
+                f[u][i] = (u < n && (FULL || c < nch)) ? __builtin_nontemporal_load(src + c)
+                                                       : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < SEG; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[i][2 * q] += __uint_as_float(f[u][i][q] << 16);
+                    acc[i][2 * q + 1] += __uint_as_float(f[u][i][q] & 0xFFFF0000u);
+                }
+    }
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (!FULL && c >= nch)
+            continue;
+        if (out) {
+            u32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[q] = (__float_as_uint(acc[i][2 * q]) >> 16) |
+                       (__float_as_uint(acc[i][2 * q + 1]) & 0xFFFF0000u);
+            out[t * nch + c] = v;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (__float_as_uint(acc[i][q]) == 0xFFFFFFFFu)
+                    *sink = 1u;
+        }
+    }
+}
+
+template <int SEG>
+void launch_gather(bool full, dim3 g, hipStream_t s, const int32_t *ros, int64_t T, int k, int64_t R,
+                   int nch, const u32x4 *y, u32x4 *o, uint32_t *sink)
+{
+    if (full)
+        hipLaunchKernelGGL((k_gather<SEG, true>), g, dim3(kWave * kWaves), 0, s, ros, T, k, R, nch, y, o, sink);
+    else
+        hipLaunchKernelGGL((k_gather<SEG, false>), g, dim3(kWave * kWaves), 0, s, ros, T, k, R, nch, y, o, sink);
 }
 
 // XCC_ID hardware register (id 20), bits [3:0]: s_getreg's immediate is
@@ -189,6 +286,36 @@ int moe_ceiling_scatter(const int32_t *row_of_slot, int64_t T, int32_t k, int64_
     case 1: hipLaunchKernelGGL(k_scatter<1>, g, b, 0, s, row_of_slot, T, k, R, nch, d); break;
     case 2: hipLaunchKernelGGL(k_scatter<2>, g, b, 0, s, row_of_slot, T, k, R, nch, d); break;
     default: hipLaunchKernelGGL(k_scatter<4>, g, b, 0, s, row_of_slot, T, k, R, nch, d); break;
+    }
+    return launched();
+}
+
+int moe_ceiling_gather(const int32_t *row_of_slot, int64_t T, int32_t k, int64_t R, int32_t H,
+                       const void *Y, void *out, uint32_t *sink, int seg_kib, void *stream)
+{
+    if (T < 0 || k < 1 || k > kWave || R < 0 || H <= 0 || H % 256 != 0 ||
+        (seg_kib != 1 && seg_kib != 2 && seg_kib != 4))
+        return MOE_CEILING_ERR_ARG;
+    if (T == 0)
+        return MOE_CEILING_OK;
+    if (!row_of_slot || (R > 0 && (!Y || !aligned16(Y))) || (out && !aligned16(out)) ||
+        (!out && !sink))
+        return MOE_CEILING_ERR_ARG;
+    const int nch = H / 8;
+    const int span = seg_kib * kWave;
+    const int64_t waves = T * ((nch + span - 1) / span);
+    const int64_t nb = (waves + kWaves - 1) / kWaves;
+    if (nb > kMaxBlocks)
+        return MOE_CEILING_ERR_ARG;
+    const bool full = nch % span == 0;
+    const dim3 g(static_cast<unsigned>(nb));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *y = static_cast<const u32x4 *>(Y);
+    u32x4 *o = static_cast<u32x4 *>(out);
+    switch (seg_kib) {
+    case 1: launch_gather<1>(full, g, s, row_of_slot, T, k, R, nch, y, o, sink); break;
+    case 2: launch_gather<2>(full, g, s, row_of_slot, T, k, R, nch, y, o, sink); break;
+    default: launch_gather<4>(full, g, s, row_of_slot, T, k, R, nch, y, o, sink); break;
     }
     return launched();
 }

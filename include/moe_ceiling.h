@@ -46,6 +46,22 @@ int moe_ceiling_copy(const void *src, void *dst, size_t bytes, int piece_kib, vo
 int moe_ceiling_scatter(const int32_t *row_of_slot, int64_t T, int32_t k, int64_t R, int32_t H,
                         void *rows, int seg_kib, void *stream);
 
+/* The combine's reads along a handle: for every token t < T, the rows of Y
+ * ([R,H] bf16, H a positive multiple of 256) that row_of_slot ([T,k] int32,
+ * 1 <= k <= 64; entries outside [0, R) skipped; a repeated row is read each
+ * time it is named) names, one wave per (token, segment of seg_kib KiB: 1, 2
+ * or 4), the segments of four named rows loaded (non-temporal) before any is
+ * added, summed in fp32 in slot order.
+ *   out   [T,H] bf16 (16-byte aligned): receives each summed segment, each
+ *         element's upper 16 bits (truncated, not rounded); or NULL for a
+ *         read-only gather that stores nothing...
+ *   sink  ...except into this int32 device word, and only when a sum has the
+ *         all-ones NaN bit pattern, which finite rows never give (it keeps
+ *         the loads alive); may be NULL when out is given.
+ * T = 0 launches nothing. */
+int moe_ceiling_gather(const int32_t *row_of_slot, int64_t T, int32_t k, int64_t R, int32_t H,
+                       const void *Y, void *out, uint32_t *sink, int seg_kib, void *stream);
+
 /* out[j] = the XCD (accelerator complex die, 0..7 on MI355X) that workgroup
  * j of a grid of `nblocks` workgroups of 256 threads (the row kernels'
  * size) ran on, from its first wave's

@@ -39,5 +39,16 @@ def test_refusals():
     assert sc(FAKE, 10, 8, 100, 256, FAKE, 3, None) == C.ERR_ARG          # segment size
     assert sc(FAKE, -1, 8, 100, 256, FAKE, 1, None) == C.ERR_ARG
     assert sc(None, 0, 8, 100, 256, None, 1, None) == C.OK                # no token
+    ga = L.moe_ceiling_gather
+    assert ga(FAKE, 10, 8, 100, 300, FAKE, FAKE, None, 2, None) == C.ERR_ARG   # H % 256
+    assert ga(FAKE, 10, 0, 100, 256, FAKE, FAKE, None, 2, None) == C.ERR_ARG   # k
+    assert ga(FAKE, 10, 65, 100, 256, FAKE, FAKE, None, 2, None) == C.ERR_ARG
+    assert ga(FAKE, 10, 8, 100, 256, FAKE, FAKE, None, 3, None) == C.ERR_ARG   # segment size
+    assert ga(None, 10, 8, 100, 256, FAKE, FAKE, None, 2, None) == C.ERR_ARG
+    assert ga(FAKE, 10, 8, 100, 256, FAKE + 4, FAKE, None, 2, None) == C.ERR_ARG  # Y misaligned
+    assert ga(FAKE, 10, 8, 100, 256, FAKE, FAKE + 8, None, 2, None) == C.ERR_ARG  # out misaligned
+    assert ga(FAKE, 10, 8, 100, 256, FAKE, None, None, 2, None) == C.ERR_ARG   # read only, no sink
+    assert ga(FAKE, -1, 8, 100, 256, FAKE, FAKE, None, 2, None) == C.ERR_ARG
+    assert ga(None, 0, 8, 100, 256, None, None, None, 2, None) == C.OK          # no token
     assert L.moe_ceiling_xcd_map(None, 4, None) == C.ERR_ARG
     assert L.moe_ceiling_xcd_map(None, 0, None) == C.OK
