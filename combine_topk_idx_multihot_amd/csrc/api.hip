@@ -246,6 +246,7 @@ moe::RowArgs dispatch_args(const moe_desc *desc, const moe_handle *handle, const
     a.k = desc->k;
     a.EL = desc->num_local;
     a.E_total = desc->E;
+    a.P = desc->pad_multiple;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
     a.pairs = rows_q ? nullptr : handle_pairs(desc, handle, a.pg);
@@ -704,6 +705,7 @@ int moe_combine_bwd(const moe_desc *desc, const moe_handle *handle, const uint16
     a.k = desc->k;
     a.EL = desc->num_local;
     a.E_total = desc->E;
+    a.P = desc->pad_multiple;
     a.H = H;
     a.eager = desc->mode == MOE_EAGER;
     a.pairs = handle_pairs(desc, handle, a.pg);

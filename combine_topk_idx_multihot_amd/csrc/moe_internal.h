@@ -108,6 +108,8 @@ struct RowArgs {
     int32_t waves_per_token;   // 1, 2 or 4: a token's segments are dealt over these waves
     int32_t dot_seg;           // combine backward: chunks per lane per dot segment
     int32_t dot_wpt;           // combine backward: waves sharing one token's dots (1, 2 or 4)
+    int32_t P = 1;             // pad_multiple
+    int32_t exp_slices = 1;    // workgroups per expert group (pad rows and row_expert)
     int64_t ntok_blocks, nexp_blocks, nsent_blocks;
     int64_t ndot_blocks;       // combine backward with dw: periods of 4 tokens, 0 otherwise
     int32_t keep_tail = 0;     // eager, R = the buffers' capacity: rows past the total are

@@ -375,25 +375,34 @@ __device__ __forceinline__ void move_token(const RowArgs &a, int64_t bid)
     }
 }
 
-// Pad rows of one expert's group: zero data, token -1, weight 0; every row of
-// the group gets row_expert = e.
-__device__ __forceinline__ void fill_expert(const RowArgs &a, int e)
+// Pad rows of an expert's group: zero data, token -1, weight 0; every row of
+// the group gets row_expert = e.  Expert workgroup j takes slice j % S of
+// expert j / S (S = exp_slices): that contiguous share of the group's rows
+// and of its pad rows.
+__device__ __forceinline__ void fill_expert(const RowArgs &a, int j)
 {
+    const int S = a.exp_slices;
+    const int e = j / S;
+    const int sl = j - e * S;
     // clamped into [0, R] so that no handle content can move a write out of bounds
     const int64_t lo = max<int64_t>(0, min<int64_t>(a.off[e], a.R));
     const int64_t hi = max<int64_t>(lo, min<int64_t>(a.off[e + 1], a.R));
     const int64_t pad0 = max<int64_t>(lo, min<int64_t>(lo + a.tpe[e], hi));
+    const int64_t gs = (hi - lo + S - 1) / S;
+    const int64_t g0 = min(hi, lo + sl * gs), g1 = min(hi, g0 + gs);
+    const int64_t ps = (hi - pad0 + S - 1) / S;
+    const int64_t p0 = min(hi, pad0 + sl * ps), p1 = min(hi, p0 + ps);
     const int tid = threadIdx.x;
     if (a.row_expert)
-        for (int64_t r = lo + tid; r < hi; r += kRowThreads)
+        for (int64_t r = g0 + tid; r < g1; r += kRowThreads)
             a.row_expert[r] = e;
-    for (int64_t r = pad0 + tid; r < hi; r += kRowThreads) {
+    for (int64_t r = p0 + tid; r < p1; r += kRowThreads) {
         if (a.row_token)
             a.row_token[r] = -1;
         if (a.row_w)
             a.row_w[r] = 0.f;
     }
-    zero_rows(a, pad0, hi, threadIdx.x / kWave, kRowWaves, tid & (kWave - 1));
+    zero_rows(a, p0, p1, threadIdx.x / kWave, kRowWaves, tid & (kWave - 1));
 }
 
 // One-shot form of the sync-free tail fill: wave gw of the sentinel grid owns
@@ -1532,6 +1541,10 @@ static int64_t sentinel_blocks(const RowArgs &a)
 
 static int nch_of(const RowArgs &a) { return a.H >> 3; }
 
+#ifndef MOE_PAD_SLICE_BYTES
+#define MOE_PAD_SLICE_BYTES 65536
+#endif
+
 void row_shape(RowArgs &a)
 {
     const int whole = chunks_per_lane(a.H);
@@ -1560,7 +1573,15 @@ void row_shape(RowArgs &a)
     a.waves_per_token = nseg >= 4 && MOE_MAX_WPT >= 4 ? 4 : (nseg >= 2 && MOE_MAX_WPT >= 2 ? 2 : 1);
     const int64_t tpb = kRowWaves / a.waves_per_token;
     a.ntok_blocks = (a.T + tpb - 1) / tpb;
-    a.nexp_blocks = a.R > 0 ? a.EL : 0;
+    // Pad rows: each expert's group has at most P - 1; its workgroups share
+    // them so that none zeroes more than about 64 KiB (1 to 16 per expert).
+    // One workgroup zeroing 127 rows of 4 KiB (P = 128) ran alone at the end
+    // of the grid.
+    const int64_t row_bytes = a.rows_q ? a.H + (a.H >> 7) * 4 : static_cast<int64_t>(a.H) * 2;
+    const int64_t pad_bytes = static_cast<int64_t>(a.P > 1 ? a.P - 1 : 0) * row_bytes;
+    const int64_t sl = (pad_bytes + MOE_PAD_SLICE_BYTES - 1) / MOE_PAD_SLICE_BYTES;
+    a.exp_slices = static_cast<int32_t>(sl < 1 ? 1 : (sl > 16 ? 16 : sl));
+    a.nexp_blocks = a.R > 0 ? static_cast<int64_t>(a.EL) * a.exp_slices : 0;
     a.nsent_blocks = sentinel_blocks(a);
     // rows walked from the route's row list: the bf16 dispatch and the
     // combine backward of a handle that carries one

@@ -128,6 +128,8 @@ EDGE = [
     ("big_H", 70, 8, 3, 0, 8, 2, False, 9216, 0.1, False),
     ("empty", 0, 8, 2, 0, 8, 4, False, 256, 0.0, False),
     ("empty_sync_free", 0, 8, 2, 0, 8, 4, True, 512, 0.0, False),
+    # pad rows of 2112 bytes (codes and scales), 99 per expert over 4 workgroups
+    ("pad_slices", 300, 16, 4, 0, 16, 100, False, 2048, 0.1, False),
 ]
 
 

@@ -269,6 +269,10 @@ EDGE = [
     ("large_route_dups_bad_ids", 33000, 128, 8, 0, 128, 4, False, 256, 0.05, True, True),
     ("large_route_1024_local_132_blocks", 4200, 1024, 8, 0, 1024, 1, True, 256, 0.02, True,
      False),
+    # an expert's pad rows shared by several workgroups (at most about 64 KiB
+    # each): 99 rows of 4 KiB over 7, and 599 over the cap of 16, sync-free
+    ("pad_slices_uneven", 300, 16, 4, 0, 16, 100, False, 2048, 0.1, False, False),
+    ("pad_slices_capped_sync_free", 200, 8, 2, 0, 8, 600, True, 2048, 0.05, True, False),
 ]
 
 
