@@ -1,7 +1,8 @@
 // ceiling.hip -- reference kernels that bound what MI355X's memory gives for
 // the access patterns of libmoe_mi355x's row kernels (declared in
-// include/moe_ceiling.h).  They compute nothing of the method; a benchmark
-// times them beside the library's kernels on the same buffers.
+// include/moe_ceiling.h).  They are not the method's path (the gather's sum
+// truncates to bf16); a benchmark times them beside the library's kernels on
+// the same buffers.
 //
 //   fill     one-shot zero fill in address order: wave g writes piece g
 //            (piece_kib KiB) with non-temporal 16-byte stores and exits, so

@@ -3,10 +3,13 @@
  * the MI355X memory system gives for its access patterns
  * (libmoe_ceiling.so).
  *
- * They compute nothing of the MoE method.  A benchmark times them on the same
- * GPU, on buffers of the same sizes and, for the scatter, along the same
- * handle, and reports each library kernel's rate as a fraction of the
- * matching reference: a practical ceiling beside the 8 TB/s HBM peak.
+ * They are not part of the MoE method's path: they move the same bytes in
+ * the same patterns (the gather also sums its rows, truncating to bf16, as a
+ * stand-in for the combine's arithmetic).  A benchmark times them on the same
+ * GPU, on buffers of the same sizes and, for the scatter and the gather,
+ * along the same handle, and reports each library kernel's rate as a fraction
+ * of the matching reference: a practical ceiling (for the gather, a
+ * reference) beside the 8 TB/s HBM peak.
  *
  * Conventions: device pointers on the current device, 16-byte aligned;
  * `stream` is a hipStream_t passed as void* (NULL = the null stream); every
