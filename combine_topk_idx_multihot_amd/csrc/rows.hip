@@ -31,16 +31,17 @@
 //     row otherwise) end each wave's part, and the token's first wave adds
 //     the parts in wave order through LDS before the single rounding to fp32,
 //     so dw is the same on every run.
-//   * pad rows are zeroed by extra workgroups of the rows' launch (one per
-//     expert).  The sync-free tail [total, R) -- most of the bytes when the
-//     worst case is far from the routed total -- is a launch of its own just
-//     before, of one-shot waves that each zero one 1 KiB piece in address
-//     order: the writes in flight then form one window sliding through the
-//     tail, which MI355X's HBM takes markedly faster than the same writes
-//     spread over the range.  In eager mode the tail is normally empty; a few
-//     workgroups of the rows' launch cover it in 64 KiB wave tasks.  A
-//     sync-free worst case of at most 32 MiB of rows (decode sizes) is zeroed
-//     the same way, by workgroups of the rows' launch, saving a launch.
+//   * pad rows are zeroed by extra workgroups of the rows' launch (1 to 16
+//     per expert, about 64 KiB of pad rows each).  The sync-free tail
+//     [total, R) -- most of the bytes when the worst case is far from the
+//     routed total -- is a launch of its own just before, of one-shot waves
+//     that each zero one 1 KiB piece in address order: the writes in flight
+//     then form one window sliding through the tail, which MI355X's HBM
+//     takes markedly faster than the same writes spread over the range.  In
+//     eager mode the tail is normally empty; a few workgroups of the rows'
+//     launch cover it in 64 KiB wave tasks.  A sync-free worst case of at
+//     most 32 MiB of rows (decode sizes) is zeroed the same way, by
+//     workgroups of the rows' launch, saving a launch.
 //   * combine adds the token's rows in fp32 in ascending slot order (the
 //     accumulator starts from the first row) and writes bf16 (nearest-even)
 //     or fp32; one wave per (token, segment).
